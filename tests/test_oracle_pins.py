@@ -1,0 +1,319 @@
+"""Pins of the CPU oracle against what the sources and mathematics fix.
+
+No page prints a worked example or an output value of the MoE layer, so the oracle is
+pinned by: library routines for the special cases that reduce to them (numpy fp64 matmul,
+torch's tanh-GeLU, scipy's softmax, numpy's stable argsort), closed forms (identity
+experts, x = 0), brute-force enumeration (top-k), an fp64 brute force for rounding, and
+invariants of the layer (padding, token permutation, expert relabelling, batch
+invariance, linearity in the down/up scales). Each test names the mistake it catches.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+import synth
+
+
+def bf(a):
+    return synth.bf16_bits_to_f32(a).astype(np.float64)
+
+
+def rms(a):
+    return float(np.sqrt(np.mean(np.asarray(a, np.float64) ** 2)))
+
+
+def small(name, T=16, d=48, f=80, E=4, k=2, **kw):
+    return synth.make_inputs(synth.custom(name, T=T, d=d, f=f, E=E, k=k, **kw))
+
+
+def gelu_ref(v):
+    return torch.nn.functional.gelu(torch.as_tensor(v, dtype=torch.float64), approximate="tanh").numpy()
+
+
+def numpy_layer(inp, ids, w):
+    """The layer written with numpy fp64 matmuls and torch's tanh-GeLU, given a routing."""
+    x = bf(inp["x"])
+    E, d, f = inp["w_gate"].shape
+    s = bf(inp["scales"])
+    out = np.zeros((x.shape[0], d))
+    for t in range(x.shape[0]):
+        if inp["pad_mask"] is not None and inp["pad_mask"][t] == 0:
+            continue
+        for j in range(ids.shape[1]):
+            e = ids[t, j]
+            Wg = inp["w_gate"][e].astype(np.float64) * s[e, :f][None, :]
+            Wu = inp["w_up"][e].astype(np.float64) * s[e, f:2 * f][None, :]
+            Wd = inp["w_down"][e].astype(np.float64) * s[e, 2 * f:][None, :]
+            h = gelu_ref(x[t] @ Wg) * (x[t] @ Wu)
+            out[t] += float(w[t, j]) * (h @ Wd)
+    return out
+
+
+# ---------------------------------------------------------------- GeLU (expert step 3)
+
+def test_gelu_is_the_tanh_form():
+    v = np.linspace(-8, 8, 2001).astype(np.float32)
+    ours = np.array([oracle.gelu_tanh(float(a)) for a in v], np.float64)
+    ref = gelu_ref(v.astype(np.float64))
+    # fp32 rounding: relative 1e-5, plus ~|v| ulp where 1 + tanh cancels for v << 0
+    assert np.all(np.abs(ours - ref) <= 1e-5 * np.abs(ref) + 2e-7 * np.maximum(1, np.abs(v)))
+    # and not the erf form (catches the wrong GeLU variant): they differ by up to ~1e-3
+    erf = torch.nn.functional.gelu(torch.as_tensor(v, dtype=torch.float64)).numpy()
+    assert np.max(np.abs(ours - erf)) > 1e-4
+
+
+def test_gelu_identities():
+    # gelu(v) - gelu(-v) = v exactly in real arithmetic (the tanh term is odd); gelu(0) = 0
+    for v in [0.1, 0.5, 1.0, 2.5, 7.0]:
+        assert abs(oracle.gelu_tanh(v) - oracle.gelu_tanh(-v) - v) < 4e-7 * max(1, v)
+    assert oracle.gelu_tanh(0.0) == 0.0
+    assert abs(oracle.gelu_tanh(10.0) - 10.0) < 1e-6 and abs(oracle.gelu_tanh(-10.0)) < 1e-6
+
+
+# ---------------------------------------------------------------- router (steps 1-2)
+
+def test_router_logits_and_softmax_vs_library():
+    inp = small("route-lib", T=64, d=200, E=8, bias=(0.3, -0.2, 0, 0, 1.0, 0, 0, -0.5))
+    r = oracle.route(inp["x"], inp["router_w"], inp["router_bias"], None, k=2)
+    ref_logits = bf(inp["x"]) @ inp["router_w"].astype(np.float64) + np.asarray(inp["router_bias"])
+    bound = 200 * 2.0 ** -23 * (np.abs(bf(inp["x"])) @ np.abs(inp["router_w"].astype(np.float64))) + 1e-7
+    assert np.all(np.abs(r["logits"] - ref_logits) <= bound)  # catches a dropped bias or wrong W index
+    p_ref = scipy.special.softmax(r["logits"].astype(np.float64), axis=1)
+    assert np.max(np.abs(r["probs"] - p_ref)) < 2e-7
+    assert np.all(np.abs(r["probs"].astype(np.float64).sum(1) - 1) <= 8 * 2.0 ** -23)
+
+
+def test_router_x_zero_pins_tie_rule():
+    # x = 0 => every logit is 0 => p = 1/E for all => ids (0, 1), w = (1/E, 1/E)
+    inp = small("route-zero", T=4, d=32, E=8)
+    x0 = np.zeros_like(inp["x"])
+    r = oracle.route(x0, inp["router_w"], None, None, k=2)
+    assert np.all(r["probs"] == np.float32(1 / 8))
+    assert np.array_equal(r["ids"], np.tile([0, 1], (4, 1)))
+    assert np.all(r["w"] == np.float32(1 / 8))
+    assert np.all(r["gap_sel"] == 0) and np.all(r["gap_order"] == 0)
+
+
+def test_top_k_equals_brute_force_enumeration():
+    # top-k by "(p desc, index asc)" equals the max-sum k-subset, lexicographically lowest on
+    # ties, listed by p desc (catches selection on the wrong end, off-by-one, or no tie rule)
+    for k, E in [(2, 8), (3, 8), (1, 4), (4, 4)]:
+        inp = small(f"topk-{k}-{E}", T=200, d=16, E=E, k=k)
+        # force exact ties: experts 1 and 2 share a router column
+        wr = inp["router_w"].copy()
+        wr[:, 2] = wr[:, 1]
+        r = oracle.route(inp["x"], wr, None, None, k=k)
+        for t in range(200):
+            p = r["probs"][t].astype(np.float64)
+            best = max(itertools.combinations(range(E), k),
+                       key=lambda c: (sum(p[list(c)]), [-i for i in c]))
+            got = r["ids"][t]
+            assert sorted(got) == sorted(best), (t, got, best)
+            assert all(p[got[j]] >= p[got[j + 1]] for j in range(k - 1))
+            assert np.array_equal(r["w"][t], r["probs"][t][got])  # weights = selected probabilities
+            if 1 in got and 2 in got:
+                assert list(got).index(1) < list(got).index(2)  # equal p: lower index first
+
+
+def test_routing_weights_are_unrenormalised_top2_probabilities(tiny_inputs):
+    r = oracle.route(tiny_inputs["x"], tiny_inputs["router_w"], None, None, k=2)
+    w, p, ids = r["w"], r["probs"], r["ids"]
+    assert np.array_equal(w, np.take_along_axis(p, ids, 1))
+    assert np.all(w.sum(1) < 1) and np.all(w[:, 0] >= w[:, 1])
+    others = p.copy()
+    np.put_along_axis(others, ids, -1, 1)
+    assert np.all(w[:, 1] >= others.max(1))
+
+
+def test_padded_tokens_get_no_route():
+    inp = small("route-pad", T=10, d=16, E=4, n_pad=3)
+    r = oracle.route(inp["x"], inp["router_w"], None, inp["pad_mask"], k=2)
+    pad = inp["pad_mask"] == 0
+    assert np.all(r["ids"][pad] == -1) and np.all(r["w"][pad] == 0)
+    assert np.all(r["ids"][~pad] >= 0)
+
+
+# ---------------------------------------------------------------- dispatch
+
+@pytest.mark.parametrize("T,E,k,n_pad", [(64, 8, 2, 0), (300, 8, 2, 70), (33, 5, 3, 4), (9, 1, 1, 0),
+                                         (0, 8, 2, 0), (5, 8, 2, 5)])
+def test_dispatch_equals_stable_argsort(T, E, k, n_pad):
+    rng = np.random.default_rng(T * 31 + E)
+    ids = np.array([rng.permutation(E)[:k] for _ in range(T)], dtype=np.int32).reshape(T, k)
+    pad = None
+    if n_pad:
+        pad = np.ones(T, np.uint8)
+        pad[rng.choice(T, n_pad, replace=False)] = 0
+    got = oracle.dispatch(ids, pad, E)
+    real = np.ones(T, bool) if pad is None else pad.astype(bool)
+    tt, jj = np.nonzero(np.broadcast_to(real[:, None], (T, k)))
+    ex = ids[tt, jj]
+    order = np.argsort(ex, kind="stable")  # library stable sort of the (t, j) pairs by expert
+    assert np.array_equal(got["perm"], tt[order])
+    assert np.array_equal(got["counts"], np.bincount(ex, minlength=E))
+    assert np.array_equal(got["offsets"], np.concatenate([[0], np.cumsum(np.bincount(ex, minlength=E))]))
+    pos = -np.ones((T, k), np.int64)
+    pos[tt[order], jj[order]] = np.arange(order.size)
+    assert np.array_equal(got["pos"], pos)
+
+
+def test_dispatch_rejects_bad_ids():
+    with pytest.raises(ValueError):
+        oracle.dispatch(np.array([[0, 9]], np.int32), None, 8)
+
+
+# ---------------------------------------------------------------- expert FFN (step 3)
+
+@pytest.mark.parametrize("d,f", [(24, 40), (40, 24)])
+def test_single_expert_is_the_dense_gated_mlp(d, f):
+    # E = k = 1 => p = 1 => out = (gelu(x Wg) * (x Wu)) Wd, checked against numpy fp64 matmuls.
+    # d != f and per-channel scale factors catch a transposed weight or a wrong scale index;
+    # swapping gate and up, or a dropped scale, fails by far more than the bound.
+    inp = small(f"dense-{d}-{f}", T=12, d=d, f=f, E=1, k=1, scale_jitter=True)
+    out, ids, w = oracle.forward_inputs(inp, k=1)
+    assert np.all(ids == 0) and np.all(w == 1.0)
+    ref = numpy_layer(inp, ids, w)
+    assert np.max(np.abs(out - ref)) <= 1e-5 * rms(ref)
+    swapped = dict(inp, w_gate=inp["w_up"], w_up=inp["w_gate"])
+    assert np.max(np.abs(numpy_layer(swapped, ids, w) - ref)) > 1e-2 * rms(ref)
+
+
+def test_hidden_and_down_stages_vs_numpy():
+    inp = small("stages", T=20, d=64, f=96, E=3, scale_jitter=True)
+    s = bf(inp["scales"])
+    x = bf(inp["x"])
+    for e in range(3):
+        h, g, u = oracle.expert_hidden(inp["x"], inp["w_gate"], inp["w_up"], inp["scales"], e, with_gu=True)
+        gr = x @ (inp["w_gate"][e] * s[e, :96])
+        ur = x @ (inp["w_up"][e] * s[e, 96:192])
+        assert np.max(np.abs(g - gr)) <= 1e-5 * rms(gr) and np.max(np.abs(u - ur)) <= 1e-5 * rms(ur)
+        assert np.max(np.abs(h - gelu_ref(gr) * ur)) <= 1e-5 * rms(h)
+        y = oracle.expert_down(h, inp["w_down"], inp["scales"], e)
+        yr = h.astype(np.float64) @ (inp["w_down"][e] * s[e, 192:])
+        assert np.max(np.abs(y - yr)) <= 1e-5 * rms(yr)
+
+
+def test_identity_experts_closed_form():
+    # d = f, q = 64 I and s = 2^-6 (both exact in int8 / bf16) => every expert matrix is I, so
+    # out[t] = (w0 + w1) * gelu(x) * x elementwise, exactly in real arithmetic.
+    T, d, E = 16, 32, 4
+    inp = small("identity", T=T, d=d, f=d, E=E)
+    eye = (64 * np.eye(d)).astype(np.int8)
+    for name in ("w_gate", "w_up", "w_down"):
+        inp[name] = np.ascontiguousarray(np.broadcast_to(eye, (E, d, d)))
+    inp["scales"] = np.full((E, 3 * d), synth.f32_to_bf16_bits(np.float32([2.0 ** -6]))[0], np.uint16)
+    out, ids, w = oracle.forward_inputs(inp)
+    x = bf(inp["x"])
+    ref = w.astype(np.float64).sum(1, keepdims=True) * gelu_ref(x) * x
+    assert np.max(np.abs(out - ref)) <= 4e-7 * np.max(np.abs(ref)) + 1e-30
+
+
+def test_zero_input_gives_zero_output():
+    inp = small("zero", T=6, d=16, f=24)
+    inp["x"] = np.zeros_like(inp["x"])
+    out, ids, w = oracle.forward_inputs(inp)
+    assert np.all(out == 0) and np.array_equal(ids, np.tile([0, 1], (6, 1)))
+
+
+def test_down_and_up_scales_are_linear():
+    # doubling every down (or up) scale doubles out bit-exactly (powers of two are exact)
+    inp = small("lin", T=16, d=32, f=48, E=4)
+    out, _, _ = oracle.forward_inputs(inp)
+    for sl in (slice(96, None), slice(48, 96)):
+        s2 = bf(inp["scales"]).astype(np.float32)
+        s2[:, sl] *= 2
+        out2, _, _ = oracle.forward_inputs(dict(inp, scales=synth.f32_to_bf16_bits(s2)))
+        assert np.array_equal(out2, 2 * out)
+
+
+# ---------------------------------------------------------------- the layer (steps 1-4)
+
+@pytest.mark.parametrize("kw", [dict(), dict(n_pad=5), dict(k=3), dict(bias=(1.0, 0.0, -1.0, 0.5)),
+                                dict(x_dist="student4", scale_jitter=True)])
+def test_sparse_equals_dense_one_hot_formulation(kw):
+    # the pages' own formulation: all experts on all tokens, combined with one-hot masks x gate
+    inp = small("dense-vs-sparse", T=24, d=40, f=56, E=4, **kw)
+    k = kw.get("k", 2)
+    out, _, _ = oracle.forward_inputs(inp, k=k)
+    dense = oracle.forward_dense(inp["x"], inp["router_w"], inp["router_bias"], inp["w_gate"], inp["w_up"],
+                                 inp["w_down"], inp["scales"], inp["pad_mask"], k=k)
+    assert np.max(np.abs(out - dense)) <= 1e-5 * rms(dense)
+    if k == 2:
+        assert np.array_equal(out, dense)  # two terms: addition order cannot matter
+
+
+def test_fp32_oracle_within_rounding_of_fp64_brute_force(tiny_inputs):
+    for inp in [small("bf-a", T=8, d=16, f=16, E=4), small("bf-b", T=8, d=12, f=8, E=3, n_pad=2),
+                tiny_inputs]:
+        out, ids, _ = oracle.forward_inputs(inp)
+        ref, ids64 = oracle.forward_f64(inp["x"][:16], inp["router_w"], inp["router_bias"], inp["w_gate"],
+                                        inp["w_up"], inp["w_down"], inp["scales"],
+                                        None if inp["pad_mask"] is None else inp["pad_mask"][:16])
+        assert np.array_equal(ids[:16], ids64)
+        assert np.max(np.abs(out[:16] - ref)) <= 1e-5 * rms(ref)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("d,f", [(6144, 64), (64, 32768)])
+def test_fp32_oracle_error_at_grok_contraction_lengths(d, f):
+    # the two long sums of the real layer: K = 6144 (gate/up) and K = 32768 (down)
+    inp = small(f"long-{d}-{f}", T=4, d=d, f=f, E=2)
+    out, ids, _ = oracle.forward_inputs(inp)
+    ref, ids64 = oracle.forward_f64(inp["x"], inp["router_w"], None, inp["w_gate"], inp["w_up"],
+                                    inp["w_down"], inp["scales"], None)
+    assert np.array_equal(ids, ids64)
+    assert np.max(np.abs(out - ref)) <= 1e-4 * rms(ref)
+
+
+def test_padded_rows_are_zero_and_do_not_affect_real_rows():
+    inp = small("pad-inv", T=20, d=32, f=48, n_pad=6)
+    out, ids, _ = oracle.forward_inputs(inp)
+    pad = inp["pad_mask"] == 0
+    assert np.all(out[pad] == 0) and not np.any(np.signbit(out[pad]))
+    x2 = inp["x"].copy()
+    x2[pad] = synth.f32_to_bf16_bits(np.full((pad.sum(), 32), 1000.0, np.float32))
+    out2, _, _ = oracle.forward_inputs(dict(inp, x=x2))
+    assert np.array_equal(out2, out)
+
+
+def test_token_permutation_commutes(tiny_inputs):
+    out, _, _ = oracle.forward_inputs(tiny_inputs)
+    perm = np.random.default_rng(1).permutation(64)
+    outp, _, _ = oracle.forward_inputs(dict(tiny_inputs, x=np.ascontiguousarray(tiny_inputs["x"][perm])))
+    assert np.array_equal(outp, out[perm])
+
+
+def test_expert_relabelling():
+    inp = small("relabel", T=32, d=32, f=40, E=4, bias=(0.1, 0.2, 0.3, 0.4))
+    out, ids, _ = oracle.forward_inputs(inp)
+    sigma = np.array([2, 0, 3, 1])  # new expert i is old expert sigma[i]
+    inv = np.argsort(sigma)
+    relab = dict(inp, router_w=np.ascontiguousarray(inp["router_w"][:, sigma]),
+                 router_bias=np.ascontiguousarray(np.asarray(inp["router_bias"], np.float32)[sigma]),
+                 scales=np.ascontiguousarray(inp["scales"][sigma]))
+    for name in ("w_gate", "w_up", "w_down"):
+        relab[name] = np.ascontiguousarray(inp[name][sigma])
+    out2, ids2, _ = oracle.forward_inputs(relab)
+    assert np.array_equal(ids2, inv[ids])
+    # the softmax denominator is summed in expert order, so relabelling moves w by an ulp
+    assert np.max(np.abs(out2 - out)) <= 1e-6 * rms(out)
+
+
+def test_batch_invariance_and_thread_count_independence(tiny_inputs):
+    out, _, _ = oracle.forward_inputs(tiny_inputs, nthreads=1)
+    out8, _, _ = oracle.forward_inputs(tiny_inputs, nthreads=8)
+    assert np.array_equal(out, out8)
+    for t in (0, 17, 63):
+        one, _, _ = oracle.forward_inputs(tiny_inputs, rows=[t])
+        assert np.array_equal(one[0], out[t])
+
+
+def test_empty_batch():
+    inp = small("empty", T=0, d=16, f=16)
+    out, ids, w = oracle.forward_inputs(inp)
+    assert out.shape == (0, 16) and ids.shape == (0, 2)
