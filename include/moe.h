@@ -1,0 +1,153 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) forward pass of Grok-1's top-2-of-8
+ * Mixture-of-Experts feed-forward layer (MoELayer + Router).
+ *
+ * The operation (Grok-1 Admin & Architecture Guide, section 3 "The Model",
+ * subsection "Mixture of Experts (MoELayer + Router)", steps 1-4; subsection
+ * "Quantized weights"; section 9 for fp32 routing):
+ *
+ *   l[t,e]  = sum_i x[t,i] * router_w[i,e] (+ router_bias[e])         fp32
+ *   p[t,:]  = softmax(l[t,:])                                          fp32
+ *   ids[t]  = the k experts of largest p (ties -> lower index), slot 0 largest
+ *   w[t,j]  = p[t, ids[t,j]]                                (not renormalised)
+ *   for each selected expert e = ids[t,j]:
+ *     g = x[t] (q_gate[e] * s_gate[e]),  u = x[t] (q_up[e] * s_up[e])
+ *     h = gelu_tanh(g) * u
+ *     y = h (q_down[e] * s_down[e])
+ *   out[t]  = sum_j w[t,j] * y_(t,j);   padded tokens: ids -1, w 0, out row +0.0
+ *
+ * The expert FFN is the gated GeLU MLP gelu(linear(x)) * linear_v(x) -> linear_1 of
+ * step 3; the weights are int8 with one bf16 scale per output channel, dequantised as
+ * q * s (section 3 "Quantized weights"). GeLU is the tanh form. The layer is
+ * token-wise, so a [B, S, d] activation is passed flattened as T = B * S rows; the
+ * caller applies the pre-norm and the residual add around it (grok-field-guide source
+ * map, fourth stop: moe(rms_norm(h), padding_mask) added to h).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE memory owned by the caller, row-major, and must
+ *     stay valid until the work enqueued on `stream` completes. Pointers to vector data
+ *     must be 16-byte aligned (x, weights, scales, out, h, y). The library never frees
+ *     or retains a caller pointer beyond the call.
+ *   - `stream` is a hipStream_t (NULL = the default stream). All work is enqueued
+ *     asynchronously; no entry point synchronises the host with the device, except the
+ *     first call on a device that needs the library workspace (hipMalloc).
+ *   - dtypes: x bf16 [T][d]; router_w fp32 [d][E]; router_bias fp32 [E];
+ *     w_gate, w_up int8 [E][d][f]; w_down int8 [E][f][d];
+ *     scales bf16 [E][2f + d] = per expert gate[f] | up[f] | down[d];
+ *     pad_mask uint8 [T] (1 = real token, 0 = padded) or NULL = all real;
+ *     out fp32 [T][d].
+ *   - Every argument is checked before anything is enqueued. On error nothing is
+ *     enqueued, outputs are untouched and a message is available from
+ *     moe_last_error() (per thread). Errors:
+ *       MOE_ERR_INVALID      a required pointer is NULL or misaligned; T < 0;
+ *                            d, f, E or k <= 0; k > E; a workspace that is too small
+ *       MOE_ERR_UNSUPPORTED  E > 64; d or f not a multiple of 256; T * max(d, f) * k
+ *                            too large for 32-bit row indexing
+ *       MOE_ERR_HIP          a HIP launch or copy failed (message holds HIP's string)
+ *       MOE_ERR_NOMEM        the library workspace could not be allocated
+ *     T == 0 is a successful no-op. Device faults surface at the caller's next sync.
+ *   - The library workspace is one buffer per device, grown on demand and shared by
+ *     all calls on that device: calls that overlap in time on one device (different
+ *     streams, different threads) race unless each passes its own workspace through
+ *     moe_forward_ex.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_HIP = 3,
+  MOE_ERR_NOMEM = 4
+} moe_status;
+
+/* Optional device outputs of the routing and dispatch steps (NULL member = not wanted).
+   topk_ids int32 [T][k]; topk_w fp32 [T][k]; counts int32 [E]; offsets int32 [E+1];
+   perm int32 [T*k] (first offsets[E] entries valid); pos int32 [T][k]. */
+typedef struct {
+  int32_t* topk_ids;
+  float* topk_w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* pos;
+} moe_debug_out;
+
+/* The layer forward pass (steps 1-4 above), without router bias. */
+int moe_forward(const void* x, const float* router_w, const int8_t* w_gate, const int8_t* w_up,
+                const int8_t* w_down, const void* scales, const uint8_t* pad_mask, float* out,
+                int T, int d, int f, int E, int k, void* stream);
+
+/* Same as moe_forward, plus:
+   router_bias  fp32 [E] added to the logits before the softmax, or NULL;
+   workspace    caller-owned device buffer of at least moe_workspace_bytes(T, d, f, E, k)
+                bytes (256-byte aligned), or NULL to use the library workspace;
+   dbg          optional copies of the routing and dispatch arrays, or NULL. */
+int moe_forward_ex(const void* x, const float* router_w, const int8_t* w_gate, const int8_t* w_up,
+                   const int8_t* w_down, const void* scales, const uint8_t* pad_mask, float* out,
+                   int T, int d, int f, int E, int k, void* stream, const float* router_bias,
+                   void* workspace, size_t workspace_bytes, const moe_debug_out* dbg);
+
+/* Step 1-2 alone: router logits, softmax and top-k (Guide section 3, MoE steps 1-2).
+   Writes topk_ids int32 [T][k] and topk_w fp32 [T][k]; padded tokens get -1 and 0. */
+int moe_route(const void* x, const float* router_w, const float* router_bias,
+              const uint8_t* pad_mask, int32_t* topk_ids, float* topk_w, int T, int d, int E,
+              int k, void* stream);
+
+/* Dispatch: a stable counting sort of the (token, slot) assignments by expert, the
+   gather that replaces the one-hot selection of the dense formulation (Guide section 3,
+   warning under the MoE steps; section 10, first item). counts[e] = assignments of real
+   tokens to e; offsets = exclusive prefix sum [E+1]; perm[offsets[e] + r] = the r-th
+   smallest token routed to e; pos[t][j] = index of (t, j) in perm. pos is -1 for padded
+   tokens and for slots whose id is out of [0, E) or repeats an earlier slot of the same
+   token (such slots are not counted). Integer work; bit-exact. */
+int moe_dispatch(const int32_t* topk_ids, const uint8_t* pad_mask, int32_t* counts,
+                 int32_t* offsets, int32_t* perm, int32_t* pos, int T, int E, int k, void* stream);
+
+/* Step 3, first half, for every expert segment of the dispatch: rows r of expert e's
+   segment take x[perm[r]]; g, u = that row times the dequantised gate / up matrices
+   (fp32 accumulation, per-output-channel scales applied in fp32); h = gelu_tanh(g) * u,
+   stored as fp16 in h [T*k][f] at row r. Rows at or beyond offsets[E] are not written. */
+int moe_gate_up(const void* x, const int32_t* perm, const int32_t* offsets, const int8_t* w_gate,
+                const int8_t* w_up, const void* scales, void* h, int T, int d, int f, int E, int k,
+                void* stream);
+
+/* Step 3, second half: y = h (q_down[e] * s_down[e]) for the rows of every expert segment,
+   with the contraction over f cut into `splits` equal parts: y fp32 [splits][T*k][d] holds
+   one partial sum per part (their sum, in part order, is the result). splits must divide
+   f / 64. moe_down_splits() gives the count moe_forward uses for a shape. */
+int moe_down(const void* h, const int32_t* offsets, const int8_t* w_down, const void* scales,
+             float* y, int splits, int T, int d, int f, int E, int k, void* stream);
+int moe_down_splits(int T, int d, int f, int E, int k);
+
+/* Step 4: out[t] = sum over j of topk_w[t][j] * (sum over parts s of y[s][pos[t][j]]),
+   parts in order, slots in order, fp32; +0.0 rows for padded tokens. */
+int moe_combine(const float* y, int splits, const int32_t* pos, const float* topk_w,
+                const uint8_t* pad_mask, float* out, int T, int d, int k, void* stream);
+
+/* Bytes of device workspace moe_forward needs for a shape (0 for T == 0). */
+size_t moe_workspace_bytes(int T, int d, int f, int E, int k);
+
+/* Frees the library workspace of every device (waits for the device first). */
+void moe_release_workspace(void);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* ABI version of this header. */
+int moe_abi_version(void);
+#define MOE_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

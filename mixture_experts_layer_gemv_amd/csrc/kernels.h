@@ -1,0 +1,41 @@
+// Host-side launchers of the MoE layer's gfx950 kernels (internal to libmoe).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// T at or below which the expert FFN takes the weight-streaming (decode) kernels.
+constexpr int kDecodeMaxT = 64;
+
+hipError_t launch_router(const uint16_t* x, const float* router_w, const float* router_bias,
+                         const uint8_t* pad_mask, int32_t* topk_ids, float* topk_w, int T, int d,
+                         int E, int k, hipStream_t stream);
+
+hipError_t launch_dispatch(const int32_t* ids, const uint8_t* pad_mask, int32_t* counts,
+                           int32_t* offsets, int32_t* perm, int32_t* pos, int T, int E, int k,
+                           hipStream_t stream);
+
+hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* perm, const int32_t* offsets,
+                                 const int8_t* w_gate, const int8_t* w_up, const uint16_t* scales,
+                                 _Float16* H, int d, int f, int E, hipStream_t stream);
+
+hipError_t launch_down_decode(const _Float16* H, const int32_t* offsets, const int8_t* w_down,
+                              const uint16_t* scales, float* Y, int splits, int rows_cap, int d,
+                              int f, int E, hipStream_t stream);
+
+hipError_t launch_gate_up_prefill(const uint16_t* x, const int32_t* perm, const int32_t* offsets,
+                                  const int8_t* w_gate, const int8_t* w_up, const uint16_t* scales,
+                                  _Float16* H, int rows_cap, int d, int f, int E, hipStream_t stream);
+
+hipError_t launch_down_prefill(const _Float16* H, const int32_t* offsets, const int8_t* w_down,
+                               const uint16_t* scales, float* Y, int splits, int rows_cap, int d,
+                               int f, int E, hipStream_t stream);
+
+hipError_t launch_combine(const float* Y, int splits, size_t part_stride, const int32_t* pos,
+                          const float* topk_w, const uint8_t* pad_mask, float* out, int T, int d,
+                          int k, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,337 @@
+// C ABI of the MoE layer (declared in include/moe.h): argument checks, workspace
+// management and the launch sequence router -> dispatch -> gate/up -> down -> combine,
+// all enqueued on the caller's stream with no host synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const std::string& msg) {
+  g_error = msg;
+  return code;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+constexpr long long kMaxAssignments = 1ll << 24;
+
+int check_shape(int T, int d, int f, int E, int k) {
+  if (T < 0) return fail(MOE_ERR_INVALID, "T must be >= 0");
+  if (d <= 0 || f <= 0 || E <= 0 || k <= 0) return fail(MOE_ERR_INVALID, "d, f, E and k must be > 0");
+  if (k > E) return fail(MOE_ERR_INVALID, "k must be <= E");
+  if (E > 64) return fail(MOE_ERR_UNSUPPORTED, "E > 64 is not supported");
+  if (d % 256 != 0 || f % 256 != 0) return fail(MOE_ERR_UNSUPPORTED, "d and f must be multiples of 256");
+  if ((long long)T * k > kMaxAssignments) return fail(MOE_ERR_UNSUPPORTED, "T * k exceeds 2^24 assignments");
+  return MOE_OK;
+}
+
+int check_ptr(const void* p, const char* name, uintptr_t align = 16) {
+  if (p == nullptr) return fail(MOE_ERR_INVALID, std::string(name) + " is NULL");
+  if (!aligned(p, align)) return fail(MOE_ERR_INVALID, std::string(name) + " is not 16-byte aligned");
+  return MOE_OK;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(MOE_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+#define MOE_TRY(expr)           \
+  do {                          \
+    int _rc = (expr);           \
+    if (_rc != MOE_OK) return _rc; \
+  } while (0)
+
+#define MOE_HIP(expr, where)                     \
+  do {                                           \
+    hipError_t _e = (expr);                      \
+    if (_e != hipSuccess) return hip_fail(_e, where); \
+  } while (0)
+
+int down_splits(int T, int f) {
+  if (T > moe::kDecodeMaxT) return 1;
+  int s = f / 4096;
+  if (s < 1) s = 1;
+  if (s > 8) s = 8;
+  while (s > 1 && (f / 64) % s != 0) s /= 2;
+  return s;
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Layout {
+  size_t ids, w, counts, offsets, perm, pos, h, y, total;
+  int splits;
+};
+
+Layout make_layout(int T, int d, int f, int E, int k) {
+  Layout L{};
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = at;
+    at += round_up(bytes, 256);
+    return o;
+  };
+  const size_t tk = (size_t)T * k;
+  L.ids = take(tk * 4);
+  L.w = take(tk * 4);
+  L.counts = take((size_t)E * 4);
+  L.offsets = take((size_t)(E + 1) * 4);
+  L.perm = take(tk * 4);
+  L.pos = take(tk * 4);
+  L.h = take(tk * f * 2);
+  L.splits = down_splits(T, f);
+  L.y = take((size_t)L.splits * tk * d * 4);
+  L.total = at;
+  return L;
+}
+
+struct DeviceWorkspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::vector<DeviceWorkspace> g_ws;
+
+int library_workspace(size_t need, char** out) {
+  int dev = 0;
+  MOE_HIP(hipGetDevice(&dev), "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
+  DeviceWorkspace& ws = g_ws[dev];
+  if (ws.bytes < need) {
+    const char* hook = std::getenv("MOE_TEST_FAIL_ALLOC");
+    if (hook && hook[0] == '1') return fail(MOE_ERR_NOMEM, "workspace allocation refused (MOE_TEST_FAIL_ALLOC=1)");
+    if (ws.ptr) {
+      MOE_HIP(hipDeviceSynchronize(), "hipDeviceSynchronize");
+      MOE_HIP(hipFree(ws.ptr), "hipFree");
+      ws.ptr = nullptr;
+      ws.bytes = 0;
+    }
+    size_t bytes = round_up(need, (size_t)1 << 20);
+    void* p = nullptr;
+    hipError_t e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(MOE_ERR_NOMEM, std::string("workspace hipMalloc of ") + std::to_string(bytes) +
+                                     " bytes failed: " + hipGetErrorString(e));
+    }
+    ws.ptr = p;
+    ws.bytes = bytes;
+  }
+  *out = static_cast<char*>(ws.ptr);
+  return MOE_OK;
+}
+
+int check_layer_args(const void* x, const float* router_w, const int8_t* w_gate, const int8_t* w_up,
+                     const int8_t* w_down, const void* scales, float* out, int T, int d, int f, int E,
+                     int k) {
+  MOE_TRY(check_shape(T, d, f, E, k));
+  MOE_TRY(check_ptr(x, "x"));
+  MOE_TRY(check_ptr(router_w, "router_w", 4));
+  MOE_TRY(check_ptr(w_gate, "w_gate"));
+  MOE_TRY(check_ptr(w_up, "w_up"));
+  MOE_TRY(check_ptr(w_down, "w_down"));
+  MOE_TRY(check_ptr(scales, "scales"));
+  MOE_TRY(check_ptr(out, "out"));
+  return MOE_OK;
+}
+
+int run_experts(const uint16_t* x, const int32_t* perm, const int32_t* offsets, const int8_t* w_gate,
+                const int8_t* w_up, const int8_t* w_down, const uint16_t* scales, _Float16* h,
+                float* y, int splits, int T, int d, int f, int E, int k, hipStream_t s) {
+  const int rows_cap = T * k;
+  if (T <= moe::kDecodeMaxT) {
+    MOE_HIP(moe::launch_gate_up_decode(x, perm, offsets, w_gate, w_up, scales, h, d, f, E, s), "gate_up");
+    MOE_HIP(moe::launch_down_decode(h, offsets, w_down, scales, y, splits, rows_cap, d, f, E, s), "down");
+  } else {
+    MOE_HIP(moe::launch_gate_up_prefill(x, perm, offsets, w_gate, w_up, scales, h, rows_cap, d, f, E, s),
+            "gate_up");
+    MOE_HIP(moe::launch_down_prefill(h, offsets, w_down, scales, y, splits, rows_cap, d, f, E, s), "down");
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_last_error(void) { return g_error.c_str(); }
+
+size_t moe_workspace_bytes(int T, int d, int f, int E, int k) {
+  if (check_shape(T, d, f, E, k) != MOE_OK || T == 0) return 0;
+  return make_layout(T, d, f, E, k).total;
+}
+
+int moe_down_splits(int T, int d, int f, int E, int k) {
+  if (check_shape(T, d, f, E, k) != MOE_OK) return 0;
+  return down_splits(T, f);
+}
+
+void moe_release_workspace(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  for (size_t dev = 0; dev < g_ws.size(); ++dev) {
+    if (!g_ws[dev].ptr) continue;
+    (void)hipSetDevice((int)dev);
+    (void)hipDeviceSynchronize();
+    (void)hipFree(g_ws[dev].ptr);
+    g_ws[dev] = DeviceWorkspace{};
+  }
+  (void)hipSetDevice(cur);
+}
+
+int moe_forward_ex(const void* x, const float* router_w, const int8_t* w_gate, const int8_t* w_up,
+                   const int8_t* w_down, const void* scales, const uint8_t* pad_mask, float* out,
+                   int T, int d, int f, int E, int k, void* stream, const float* router_bias,
+                   void* workspace, size_t workspace_bytes, const moe_debug_out* dbg) {
+  MOE_TRY(check_layer_args(x, router_w, w_gate, w_up, w_down, scales, out, T, d, f, E, k));
+  if (router_bias && !aligned(router_bias, 4)) return fail(MOE_ERR_INVALID, "router_bias is not 4-byte aligned");
+  if (T == 0) return MOE_OK;
+  const Layout L = make_layout(T, d, f, E, k);
+  char* ws = nullptr;
+  if (workspace) {
+    if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID, "workspace is not 256-byte aligned");
+    if (workspace_bytes < L.total)
+      return fail(MOE_ERR_INVALID, "workspace too small: need " + std::to_string(L.total) + " bytes");
+    ws = static_cast<char*>(workspace);
+  } else {
+    MOE_TRY(library_workspace(L.total, &ws));
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto* ids = reinterpret_cast<int32_t*>(ws + L.ids);
+  auto* w = reinterpret_cast<float*>(ws + L.w);
+  auto* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  auto* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  auto* perm = reinterpret_cast<int32_t*>(ws + L.perm);
+  auto* pos = reinterpret_cast<int32_t*>(ws + L.pos);
+  auto* h = reinterpret_cast<_Float16*>(ws + L.h);
+  auto* y = reinterpret_cast<float*>(ws + L.y);
+  const auto* xb = static_cast<const uint16_t*>(x);
+  const auto* sc = static_cast<const uint16_t*>(scales);
+
+  MOE_HIP(moe::launch_router(xb, router_w, router_bias, pad_mask, ids, w, T, d, E, k, s), "router");
+  MOE_HIP(moe::launch_dispatch(ids, pad_mask, counts, offsets, perm, pos, T, E, k, s), "dispatch");
+  MOE_TRY(run_experts(xb, perm, offsets, w_gate, w_up, w_down, sc, h, y, L.splits, T, d, f, E, k, s));
+  MOE_HIP(moe::launch_combine(y, L.splits, (size_t)T * k * d, pos, w, pad_mask, out, T, d, k, s), "combine");
+
+  if (dbg) {
+    const size_t tk = (size_t)T * k;
+    struct Copy {
+      void* dst;
+      const void* src;
+      size_t bytes;
+    } copies[] = {{dbg->topk_ids, ids, tk * 4}, {dbg->topk_w, w, tk * 4},  {dbg->counts, counts, (size_t)E * 4},
+                  {dbg->offsets, offsets, (size_t)(E + 1) * 4}, {dbg->perm, perm, tk * 4}, {dbg->pos, pos, tk * 4}};
+    for (const Copy& c : copies)
+      if (c.dst) MOE_HIP(hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyDeviceToDevice, s), "debug copy");
+  }
+  return MOE_OK;
+}
+
+int moe_forward(const void* x, const float* router_w, const int8_t* w_gate, const int8_t* w_up,
+                const int8_t* w_down, const void* scales, const uint8_t* pad_mask, float* out, int T,
+                int d, int f, int E, int k, void* stream) {
+  return moe_forward_ex(x, router_w, w_gate, w_up, w_down, scales, pad_mask, out, T, d, f, E, k, stream,
+                        nullptr, nullptr, 0, nullptr);
+}
+
+int moe_route(const void* x, const float* router_w, const float* router_bias, const uint8_t* pad_mask,
+              int32_t* topk_ids, float* topk_w, int T, int d, int E, int k, void* stream) {
+  MOE_TRY(check_shape(T, d, 256, E, k));
+  MOE_TRY(check_ptr(x, "x"));
+  MOE_TRY(check_ptr(router_w, "router_w", 4));
+  MOE_TRY(check_ptr(topk_ids, "topk_ids", 4));
+  MOE_TRY(check_ptr(topk_w, "topk_w", 4));
+  if (T == 0) return MOE_OK;
+  MOE_HIP(moe::launch_router(static_cast<const uint16_t*>(x), router_w, router_bias, pad_mask, topk_ids,
+                             topk_w, T, d, E, k, static_cast<hipStream_t>(stream)),
+          "router");
+  return MOE_OK;
+}
+
+int moe_dispatch(const int32_t* topk_ids, const uint8_t* pad_mask, int32_t* counts, int32_t* offsets,
+                 int32_t* perm, int32_t* pos, int T, int E, int k, void* stream) {
+  MOE_TRY(check_shape(T, 256, 256, E, k));
+  MOE_TRY(check_ptr(topk_ids, "topk_ids", 4));
+  MOE_TRY(check_ptr(counts, "counts", 4));
+  MOE_TRY(check_ptr(offsets, "offsets", 4));
+  MOE_TRY(check_ptr(pos, "pos", 4));
+  if (T > 0) MOE_TRY(check_ptr(perm, "perm", 4));
+  MOE_HIP(moe::launch_dispatch(topk_ids, pad_mask, counts, offsets, perm, pos, T, E, k,
+                               static_cast<hipStream_t>(stream)),
+          "dispatch");
+  return MOE_OK;
+}
+
+int moe_gate_up(const void* x, const int32_t* perm, const int32_t* offsets, const int8_t* w_gate,
+                const int8_t* w_up, const void* scales, void* h, int T, int d, int f, int E, int k,
+                void* stream) {
+  MOE_TRY(check_shape(T, d, f, E, k));
+  MOE_TRY(check_ptr(x, "x"));
+  MOE_TRY(check_ptr(perm, "perm", 4));
+  MOE_TRY(check_ptr(offsets, "offsets", 4));
+  MOE_TRY(check_ptr(w_gate, "w_gate"));
+  MOE_TRY(check_ptr(w_up, "w_up"));
+  MOE_TRY(check_ptr(scales, "scales"));
+  MOE_TRY(check_ptr(h, "h"));
+  if (T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const auto* xb = static_cast<const uint16_t*>(x);
+  const auto* sc = static_cast<const uint16_t*>(scales);
+  auto* hh = static_cast<_Float16*>(h);
+  if (T <= moe::kDecodeMaxT)
+    MOE_HIP(moe::launch_gate_up_decode(xb, perm, offsets, w_gate, w_up, sc, hh, d, f, E, s), "gate_up");
+  else
+    MOE_HIP(moe::launch_gate_up_prefill(xb, perm, offsets, w_gate, w_up, sc, hh, T * k, d, f, E, s), "gate_up");
+  return MOE_OK;
+}
+
+int moe_down(const void* h, const int32_t* offsets, const int8_t* w_down, const void* scales, float* y,
+             int splits, int T, int d, int f, int E, int k, void* stream) {
+  MOE_TRY(check_shape(T, d, f, E, k));
+  MOE_TRY(check_ptr(h, "h"));
+  MOE_TRY(check_ptr(offsets, "offsets", 4));
+  MOE_TRY(check_ptr(w_down, "w_down"));
+  MOE_TRY(check_ptr(scales, "scales"));
+  MOE_TRY(check_ptr(y, "y"));
+  if (splits < 1 || (f / 64) % splits != 0) return fail(MOE_ERR_INVALID, "splits must divide f / 64");
+  if (T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const auto* hh = static_cast<const _Float16*>(h);
+  const auto* sc = static_cast<const uint16_t*>(scales);
+  if (T <= moe::kDecodeMaxT)
+    MOE_HIP(moe::launch_down_decode(hh, offsets, w_down, sc, y, splits, T * k, d, f, E, s), "down");
+  else
+    MOE_HIP(moe::launch_down_prefill(hh, offsets, w_down, sc, y, splits, T * k, d, f, E, s), "down");
+  return MOE_OK;
+}
+
+int moe_combine(const float* y, int splits, const int32_t* pos, const float* topk_w, const uint8_t* pad_mask,
+                float* out, int T, int d, int k, void* stream) {
+  MOE_TRY(check_shape(T, d, 256, k, k));
+  MOE_TRY(check_ptr(y, "y"));
+  MOE_TRY(check_ptr(pos, "pos", 4));
+  MOE_TRY(check_ptr(topk_w, "topk_w", 4));
+  MOE_TRY(check_ptr(out, "out"));
+  if (splits < 1) return fail(MOE_ERR_INVALID, "splits must be >= 1");
+  if (T == 0) return MOE_OK;
+  MOE_HIP(moe::launch_combine(y, splits, (size_t)T * k * d, pos, topk_w, pad_mask, out, T, d, k,
+                              static_cast<hipStream_t>(stream)),
+          "combine");
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+"""The C ABI on the host: the library loads, exports what include/moe.h declares, and
+rejects bad arguments before touching the GPU (these calls never reach HIP)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import mixture_experts_layer_gemv_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+FAKE = 1 << 20  # an aligned non-NULL address; never dereferenced by the argument checks
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    names = declared_functions()
+    assert names == sorted(moe.SIGNATURES), names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (moe_[a-z_]+)\b", out))
+    missing = set(declared_functions()) - exported
+    assert not missing, missing
+    lib = moe.lib()
+    for name in declared_functions():
+        assert getattr(lib, name) is not None
+
+
+def test_abi_version():
+    assert moe.abi_version() == 1
+
+
+def rc_forward(**kw):
+    args = dict(x=FAKE, router_w=FAKE, w_gate=FAKE, w_up=FAKE, w_down=FAKE, scales=FAKE, pad_mask=None,
+                out=FAKE, T=8, d=256, f=512, E=8, k=2)
+    args.update(kw)
+    lib = moe.lib()
+    return lib.moe_forward(args["x"], args["router_w"], args["w_gate"], args["w_up"], args["w_down"],
+                           args["scales"], args["pad_mask"], args["out"], args["T"], args["d"], args["f"],
+                           args["E"], args["k"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(x=None), moe.MOE_ERR_INVALID, "x is NULL"),
+    (dict(out=None), moe.MOE_ERR_INVALID, "out is NULL"),
+    (dict(w_down=None), moe.MOE_ERR_INVALID, "w_down is NULL"),
+    (dict(x=FAKE + 2), moe.MOE_ERR_INVALID, "aligned"),
+    (dict(T=-1), moe.MOE_ERR_INVALID, "T must be"),
+    (dict(d=0), moe.MOE_ERR_INVALID, "> 0"),
+    (dict(k=0), moe.MOE_ERR_INVALID, "> 0"),
+    (dict(k=9), moe.MOE_ERR_INVALID, "k must be <= E"),
+    (dict(E=65, k=2), moe.MOE_ERR_UNSUPPORTED, "E > 64"),
+    (dict(d=200), moe.MOE_ERR_UNSUPPORTED, "multiples of 256"),
+    (dict(f=320), moe.MOE_ERR_UNSUPPORTED, "multiples of 256"),
+    (dict(T=1 << 24, k=2), moe.MOE_ERR_UNSUPPORTED, "2^24"),
+])
+def test_invalid_arguments_are_rejected_before_any_launch(kw, status, msg):
+    assert rc_forward(**kw) == status
+    assert msg in moe.last_error()
+
+
+def test_zero_tokens_is_a_no_op():
+    assert rc_forward(T=0) == moe.MOE_OK
+
+
+def test_stage_entry_points_check_arguments():
+    lib = moe.lib()
+    assert lib.moe_route(None, FAKE, None, None, FAKE, FAKE, 4, 256, 8, 2, None) == moe.MOE_ERR_INVALID
+    assert lib.moe_dispatch(FAKE, None, FAKE, FAKE, FAKE, None, 4, 8, 2, None) == moe.MOE_ERR_INVALID
+    assert lib.moe_dispatch(FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 8, 9, None) == moe.MOE_ERR_INVALID
+    assert lib.moe_down(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 4, 256, 512, 8, 2, None) == moe.MOE_ERR_INVALID
+    assert "splits" in moe.last_error()
+    assert lib.moe_combine(FAKE, 0, FAKE, FAKE, None, FAKE, 4, 256, 2, None) == moe.MOE_ERR_INVALID
+    assert lib.moe_gate_up(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 256, 512, 8, 2, None) == moe.MOE_OK
+
+
+def test_workspace_size_and_split_policy():
+    # decode shapes split the down projection's contraction; prefill shapes do not
+    assert moe.down_splits(8, 6144, 32768, 8, 2) == 8
+    assert moe.down_splits(64, 6144, 32768, 8, 2) == 8
+    assert moe.down_splits(65, 6144, 32768, 8, 2) == 1
+    assert moe.down_splits(64, 256, 512, 8, 2) == 1
+    tk = 16
+    need = moe.workspace_bytes(8, 6144, 32768, 8, 2)
+    assert need >= tk * 32768 * 2 + 8 * tk * 6144 * 4
+    assert moe.workspace_bytes(0, 6144, 32768, 8, 2) == 0
+    assert moe.workspace_bytes(8, 6144, 32768, 8, 9) == 0
+
+
+def test_forward_ex_rejects_small_or_misaligned_workspace():
+    lib = moe.lib()
+    need = moe.workspace_bytes(8, 256, 512, 8, 2)
+    base = [FAKE] * 6 + [None, FAKE, 8, 256, 512, 8, 2, None, None]
+    assert lib.moe_forward_ex(*base, FAKE, need - 1, None) == moe.MOE_ERR_INVALID
+    assert "too small" in moe.last_error()
+    assert lib.moe_forward_ex(*base, FAKE + 16, need, None) == moe.MOE_ERR_INVALID
+    assert "256-byte" in moe.last_error()

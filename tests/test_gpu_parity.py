@@ -1,0 +1,404 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle on the same
+seeded inputs. Integer work (ids, dispatch) bit-exact; routing weights within 1e-5;
+expert stages within their rounding; the layer output within 1e-2 * rms(ref).
+At the Grok-1 shapes the oracle computes sampled rows (rows are independent); routing and
+dispatch are compared on every token."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_helpers import (OUT_TOL, W_TOL, check_dispatch_valid, compare_ids, exclusions, fp16_from_normal, rms,
+                         sample_rows, to_dev)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - collected on CPU, skipped there
+    pytest.skip("no GPU", allow_module_level=True)
+
+import mixture_experts_layer_gemv_amd as moe  # noqa: E402
+
+CONFIG_NAMES = ["tiny", "decode", "batched_decode", "prefill", "skewed"]
+SAMPLE = {"tiny": 64, "decode": 8, "batched_decode": 16, "prefill": 16, "skewed": 16}
+
+_cache: dict = {}
+
+
+def grok_weights():
+    """Host + device copies of the weight set shared by the Grok-shape workloads."""
+    if "grok" not in _cache:
+        spec = synth.CONFIGS["decode"]
+        host = {n: synth.expert_weights(spec, n.split("_")[1]) for n in ("w_gate", "w_up", "w_down")}
+        host["router_w"] = synth.router_w(spec)
+        host["scales"] = synth.scales(spec)
+        dev = {n: torch.from_numpy(host[n]).cuda() for n in ("w_gate", "w_up", "w_down", "router_w")}
+        dev["scales"] = torch.from_numpy(host["scales"].view(np.int16)).cuda().view(torch.bfloat16)
+        _cache["grok"] = (host, dev)
+    return _cache["grok"]
+
+
+def workload(name: str):
+    """(host inputs, device inputs) of a named workload."""
+    key = ("wl", name)
+    if key not in _cache:
+        spec = synth.CONFIGS[name]
+        if spec.d == 6144:
+            host_w, dev_w = grok_weights()
+            inp = synth.make_inputs(spec, with_weights=False)
+            inp.update({n: host_w[n] for n in ("w_gate", "w_up", "w_down")})
+            d = to_dev(inp, with_weights=False)
+            d.update({n: dev_w[n] for n in ("w_gate", "w_up", "w_down")})
+        else:
+            inp = synth.make_inputs(spec)
+            d = to_dev(inp)
+        _cache[key] = (inp, d)
+    return _cache[key]
+
+
+def run_forward(d: dict, T: int, dd: int, f: int, E: int, k: int, out=None, workspace=None, ws_bytes=0):
+    if out is None:
+        out = torch.full((T, dd), float("nan"), dtype=torch.float32, device="cuda")
+    dbg = {
+        "topk_ids": torch.empty((T, k), dtype=torch.int32, device="cuda"),
+        "topk_w": torch.empty((T, k), dtype=torch.float32, device="cuda"),
+        "counts": torch.empty(E, dtype=torch.int32, device="cuda"),
+        "offsets": torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+        "perm": torch.full((max(T * k, 1),), -7, dtype=torch.int32, device="cuda"),
+        "pos": torch.empty((T, k), dtype=torch.int32, device="cuda"),
+    }
+    moe.moe_forward_ex(d["x"], d["router_w"], d["w_gate"], d["w_up"], d["w_down"], d["scales"], d["pad_mask"],
+                       out, T, dd, f, E, k, router_bias=d["router_bias"], workspace=workspace,
+                       workspace_bytes_=ws_bytes, dbg=dbg)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), {n: v.cpu().numpy() for n, v in dbg.items()}
+
+
+def check_layer(inp: dict, d: dict, rows=None, label=""):
+    spec_like = inp["x"].shape
+    T, dd = spec_like
+    E, _, f = inp["w_gate"].shape
+    k = inp.get("k", 2)
+    out, dbg = run_forward(d, T, dd, f, E, k)
+    r = oracle.route(inp["x"], inp["router_w"], inp["router_bias"], inp["pad_mask"], k)
+    excl, amb = exclusions(r)
+    n_cmp = compare_ids(dbg["topk_ids"], r["ids"], excl, amb)
+    keep = ~excl
+    assert np.all(np.abs(dbg["topk_w"][keep] - r["w"][keep]) <= W_TOL)
+    # dispatch: equal to the oracle's when no near tie moved an expert, valid either way
+    check_dispatch_valid(dbg["topk_ids"], inp["pad_mask"], E, dbg)
+    if not excl.any():
+        ref_disp = oracle.dispatch(r["ids"], inp["pad_mask"], E)
+        for n in ("counts", "offsets", "pos"):
+            assert np.array_equal(dbg[n], ref_disp[n]), n
+        assert np.array_equal(dbg["perm"][: ref_disp["offsets"][-1]], ref_disp["perm"])
+    # padded rows are exactly +0.0
+    if inp["pad_mask"] is not None:
+        padded = inp["pad_mask"] == 0
+        assert np.all(out[padded] == 0) and not np.any(np.signbit(out[padded]))
+    assert np.all(np.isfinite(out))
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    ref, ids_ref, _ = oracle.forward_inputs(inp, k=k, rows=rows)
+    assert np.array_equal(ids_ref, r["ids"][rows])
+    cmp_rows = ~excl[rows]
+    err = np.abs(out[rows][cmp_rows] - ref[cmp_rows])
+    scale = rms(ref)
+    ratio = float(err.max() / scale) if err.size else 0.0
+    print(f"[{label}] T={T} compared_ids={n_cmp} excluded={int(excl.sum())} order_ambiguous={int(amb.sum())} "
+          f"rows={len(rows)} max|err|/rms={ratio:.3e}", flush=True)
+    assert ratio <= OUT_TOL, ratio
+    return out, dbg, ratio
+
+
+# ------------------------------------------------------------------------------ routing
+
+@pytest.mark.parametrize("name", CONFIG_NAMES)
+def test_route_parity(name):
+    inp, d = workload(name)
+    s = synth.CONFIGS[name]
+    ids = torch.empty((s.T, s.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((s.T, s.k), dtype=torch.float32, device="cuda")
+    moe.moe_route(d["x"], d["router_w"], d["router_bias"], d["pad_mask"], ids, w, s.T, s.d, s.E, s.k)
+    torch.cuda.synchronize()
+    r = oracle.route(inp["x"], inp["router_w"], inp["router_bias"], inp["pad_mask"], s.k)
+    excl, amb = exclusions(r)
+    compare_ids(ids.cpu().numpy(), r["ids"], excl, amb)
+    wg = w.cpu().numpy()
+    assert np.all(np.abs(wg[~excl] - r["w"][~excl]) <= W_TOL)
+    print(f"[{name}] route: excluded near ties {int(excl.sum())} of {s.T}", flush=True)
+
+
+# ------------------------------------------------------------------------------ dispatch
+
+def gpu_dispatch(ids_np, pad_np, E):
+    T, k = ids_np.shape
+    ids = torch.from_numpy(np.ascontiguousarray(ids_np, np.int32)).cuda()
+    pad = None if pad_np is None else torch.from_numpy(pad_np).cuda()
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.full((max(T * k, 1),), -7, dtype=torch.int32, device="cuda")
+    pos = torch.empty((max(T, 1), k), dtype=torch.int32, device="cuda")
+    moe.moe_dispatch(ids, pad, counts, offsets, perm, pos, T, E, k)
+    torch.cuda.synchronize()
+    return {"counts": counts.cpu().numpy(), "offsets": offsets.cpu().numpy(), "perm": perm.cpu().numpy(),
+            "pos": pos.cpu().numpy()[:T]}
+
+
+@pytest.mark.parametrize("name", CONFIG_NAMES)
+def test_dispatch_parity_on_oracle_routing(name):
+    inp, _ = workload(name)
+    s = synth.CONFIGS[name]
+    r = oracle.route(inp["x"], inp["router_w"], inp["router_bias"], inp["pad_mask"], s.k)
+    got = gpu_dispatch(r["ids"], inp["pad_mask"], s.E)
+    ref = oracle.dispatch(r["ids"], inp["pad_mask"], s.E)
+    assert np.array_equal(got["counts"], ref["counts"]) and np.array_equal(got["offsets"], ref["offsets"])
+    n = int(ref["offsets"][-1])
+    assert np.array_equal(got["perm"][:n], ref["perm"]) and np.array_equal(got["pos"], ref["pos"])
+    print(f"[{name}] dispatch counts {ref['counts'].tolist()}", flush=True)
+
+
+@pytest.mark.parametrize("T,E,k,n_pad", [(1, 8, 2, 0), (1023, 8, 2, 100), (1025, 8, 2, 0), (3000, 5, 3, 17),
+                                         (200, 64, 4, 20), (50, 1, 1, 0), (40, 8, 2, 40), (8192, 8, 2, 0)])
+def test_dispatch_edge_cases(T, E, k, n_pad):
+    rng = np.random.default_rng(T + 7 * E + k)
+    ids = np.array([rng.permutation(E)[:k] for _ in range(T)], dtype=np.int32).reshape(T, k)
+    pad = None
+    if n_pad:
+        pad = np.ones(T, np.uint8)
+        pad[rng.choice(T, n_pad, replace=False)] = 0
+    got = gpu_dispatch(ids, pad, E)
+    ref = oracle.dispatch(ids, pad, E)
+    n = int(ref["offsets"][-1])
+    for nme in ("counts", "offsets", "pos"):
+        assert np.array_equal(got[nme], ref[nme]), nme
+    assert np.array_equal(got["perm"][:n], ref["perm"])
+
+
+def test_dispatch_ignores_out_of_range_and_repeated_ids():
+    ids = np.array([[0, 9], [3, 3], [-1, 2], [1, 0]], np.int32)
+    got = gpu_dispatch(ids, None, 8)
+    assert got["counts"].tolist() == [2, 1, 1, 1, 0, 0, 0, 0]
+    assert got["pos"].tolist() == [[0, -1], [4, -1], [-1, 3], [2, 1]]
+    assert got["perm"][:5].tolist() == [0, 3, 3, 2, 1]
+
+
+# ------------------------------------------------------------------------------ expert stages
+
+def segment_rows(offsets, E, per=3):
+    """A few rows of each expert segment: first, middle, last."""
+    out = {}
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            out[e] = sorted({a, (a + b) // 2, b - 1}) if per == 3 else list(range(a, b))
+    return out
+
+
+@pytest.mark.parametrize("name", CONFIG_NAMES)
+def test_gate_up_stage_parity(name):
+    inp, d = workload(name)
+    s = synth.CONFIGS[name]
+    r = oracle.route(inp["x"], inp["router_w"], inp["router_bias"], inp["pad_mask"], s.k)
+    disp = oracle.dispatch(r["ids"], inp["pad_mask"], s.E)
+    perm = torch.from_numpy(np.ascontiguousarray(disp["perm"])).cuda() if disp["perm"].size else \
+        torch.zeros(1, dtype=torch.int32, device="cuda")
+    offsets = torch.from_numpy(disp["offsets"]).cuda()
+    h = torch.full((s.T * s.k, s.f), float("nan"), dtype=torch.float16, device="cuda")
+    moe.moe_gate_up(d["x"], perm, offsets, d["w_gate"], d["w_up"], d["scales"], h, s.T, s.d, s.f, s.E, s.k)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for e, rows in segment_rows(disp["offsets"], s.E, per=3 if s.d == 6144 else 0).items():
+        hg = h[torch.tensor(rows, device="cuda")].cpu().numpy().astype(np.float64)
+        xr = np.ascontiguousarray(inp["x"][disp["perm"][rows]])
+        href = oracle.expert_hidden(xr, inp["w_gate"], inp["w_up"], inp["scales"], e).astype(np.float64)
+        err = np.abs(hg - href)
+        # fp16 rounding of h (2^-11 relative) plus fp32 accumulation order and the GeLU evaluation
+        bound = 2.0 ** -10 * np.abs(href) + 1e-4 * rms(href)
+        assert np.all(err <= bound), (e, float((err - bound).max()))
+        worst = max(worst, float((err / (np.abs(href) + 1e-3)).max()))
+    print(f"[{name}] gate_up: worst relative err {worst:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("name", CONFIG_NAMES)
+def test_down_stage_parity(name):
+    inp, d = workload(name)
+    s = synth.CONFIGS[name]
+    r = oracle.route(inp["x"], inp["router_w"], inp["router_bias"], inp["pad_mask"], s.k)
+    disp = oracle.dispatch(r["ids"], inp["pad_mask"], s.E)
+    n = int(disp["offsets"][-1])
+    h16 = fp16_from_normal(CONFIG_NAMES.index(name), (s.T * s.k, s.f))
+    offsets = torch.from_numpy(disp["offsets"]).cuda()
+    splits = moe.down_splits(s.T, s.d, s.f, s.E, s.k)
+    y = torch.full((splits, s.T * s.k, s.d), float("nan"), dtype=torch.float32, device="cuda")
+    moe.moe_down(torch.from_numpy(h16).cuda(), offsets, d["w_down"], d["scales"], y, splits, s.T, s.d, s.f, s.E, s.k)
+    torch.cuda.synchronize()
+    for e, rows in segment_rows(disp["offsets"], s.E, per=3 if s.d == 6144 else 0).items():
+        yg = y[:, torch.tensor(rows, device="cuda")].cpu().numpy().astype(np.float64).sum(0)
+        yref = oracle.expert_down(np.ascontiguousarray(h16[rows].astype(np.float32)), inp["w_down"], inp["scales"], e)
+        assert np.max(np.abs(yg - yref)) <= 1e-4 * rms(yref), e
+    assert n <= s.T * s.k
+
+
+def test_combine_stage():
+    rng = np.random.default_rng(3)
+    T, dd, k, splits = 37, 512, 2, 3
+    pos = np.array([rng.permutation(T * k)[:k] for _ in range(T)], np.int32)
+    pos[5] = -1
+    w = rng.random((T, k)).astype(np.float32)
+    pad = np.ones(T, np.uint8)
+    pad[[5, 11]] = 0
+    y = rng.standard_normal((splits, T * k, dd)).astype(np.float32)
+    out = torch.full((T, dd), float("nan"), device="cuda")
+    moe.moe_combine(torch.from_numpy(y).cuda(), splits, torch.from_numpy(pos).cuda(), torch.from_numpy(w).cuda(),
+                    torch.from_numpy(pad).cuda(), out, T, dd, k)
+    got = out.cpu().numpy()
+    ys = y.astype(np.float64).sum(0)
+    ref = np.zeros((T, dd))
+    for t in range(T):
+        if pad[t]:
+            for j in range(k):
+                ref[t] += w[t, j] * ys[pos[t, j]]
+    assert np.all(got[[5, 11]] == 0)
+    assert np.max(np.abs(got - ref)) <= 1e-6 * rms(ref)
+
+
+# ------------------------------------------------------------------------------ the layer
+
+@pytest.mark.parametrize("name", CONFIG_NAMES)
+def test_layer_parity(name):
+    inp, d = workload(name)
+    s = synth.CONFIGS[name]
+    pads = None if inp["pad_mask"] is None else np.nonzero(inp["pad_mask"] == 0)[0][:2]
+    rows = sample_rows(s.T, SAMPLE[name], seed=11, must=pads)
+    check_layer(inp, d, rows=rows, label=name)
+
+
+def small_case(name, **kw):
+    spec = synth.custom(name, **kw)
+    inp = synth.make_inputs(spec)
+    inp["k"] = spec.k
+    return inp, to_dev(inp)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=1, d=256, f=512),
+    dict(T=64, d=256, f=512, scale_jitter=True, x_dist="student4"),
+    dict(T=65, d=256, f=512, n_pad=1),
+    dict(T=300, d=256, f=512, n_pad=37, bias=(1.0, 0.5, 0, 0, 0, 0, 0, -1.0)),
+    dict(T=40, d=256, f=256, E=4, k=1),
+    dict(T=130, d=256, f=256, E=16, k=4),
+    dict(T=48, d=256, f=256, E=64, k=2),
+    dict(T=96, d=512, f=256, E=8, k=2, n_pad=10),
+    dict(T=33, d=768, f=1024, E=8, k=2, x_dist="student4"),
+    dict(T=1000, d=256, f=768, E=8, k=2, bias=(3.0, 2.0, 0, 0, 0, 0, 0, 0)),
+])
+def test_layer_edge_shapes(kw):
+    inp, d = small_case("edge", **kw)
+    check_layer(inp, d, label=str(kw))
+
+
+def test_all_tokens_padded():
+    inp, d = small_case("allpad", T=32, d=256, f=512, n_pad=32)
+    out, dbg = run_forward(d, 32, 256, 512, 8, 2)
+    assert np.all(out == 0) and not np.any(np.signbit(out))
+    assert np.all(dbg["counts"] == 0) and np.all(dbg["pos"] == -1) and np.all(dbg["topk_ids"] == -1)
+
+
+def test_zero_tokens_leaves_out_untouched():
+    inp, d = small_case("zero", T=4, d=256, f=512)
+    out = torch.full((4, 256), 3.0, device="cuda")
+    moe.moe_forward(d["x"], d["router_w"], d["w_gate"], d["w_up"], d["w_down"], d["scales"], None, out,
+                    0, 256, 512, 8, 2)
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all())
+
+
+# ------------------------------------------------------------------------------ invariants
+
+def test_run_to_run_bit_determinism():
+    for name in ("tiny", "decode"):
+        inp, d = workload(name)
+        s = synth.CONFIGS[name]
+        a, _ = run_forward(d, s.T, s.d, s.f, s.E, s.k)
+        b, _ = run_forward(d, s.T, s.d, s.f, s.E, s.k)
+        assert np.array_equal(a, b), name
+    inp, d = small_case("det-prefill", T=700, d=256, f=512, n_pad=50)
+    a, _ = run_forward(d, 700, 256, 512, 8, 2)
+    b, _ = run_forward(d, 700, 256, 512, 8, 2)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("T", [64, 500])
+def test_padded_row_content_does_not_change_real_rows(T):
+    inp, d = small_case("padinv", T=T, d=256, f=512, n_pad=T // 10)
+    a, _ = run_forward(d, T, 256, 512, 8, 2)
+    x2 = d["x"].clone()
+    padded = torch.from_numpy(inp["pad_mask"] == 0).cuda()
+    x2[padded] = 1000.0
+    d2 = dict(d, x=x2)
+    b, _ = run_forward(d2, T, 256, 512, 8, 2)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("T", [48, 400])
+def test_token_permutation_commutes(T):
+    inp, d = small_case("perm", T=T, d=256, f=512)
+    a, _ = run_forward(d, T, 256, 512, 8, 2)
+    p = np.random.default_rng(5).permutation(T)
+    d2 = dict(d, x=d["x"][torch.from_numpy(p).cuda()].contiguous())
+    b, _ = run_forward(d2, T, 256, 512, 8, 2)
+    err = np.abs(b - a[p]).max() / rms(a)
+    print(f"permutation T={T}: bit-exact={bool(np.array_equal(b, a[p]))} max|err|/rms={err:.2e}", flush=True)
+    assert err <= 1e-5
+
+
+def test_doubling_down_or_up_scales_doubles_out_exactly():
+    inp, d = small_case("lin", T=64, d=256, f=512)
+    a, _ = run_forward(d, 64, 256, 512, 8, 2)
+    for sl in (slice(1024, None), slice(512, 1024)):
+        sc = d["scales"].clone()
+        sc[:, sl] *= 2
+        b, _ = run_forward(dict(d, scales=sc), 64, 256, 512, 8, 2)
+        assert np.array_equal(b, 2 * a)
+
+
+def test_decode_and_prefill_kernels_agree():
+    # 64 tokens take the streaming kernels; the same tokens plus one padded token take the
+    # tiled ones; the real rows must agree to the output tolerance
+    inp, d = small_case("paths", T=65, d=512, f=768, n_pad=0)
+    inp64 = {n: (v[:64] if n == "x" else v) for n, v in inp.items()}
+    a, _ = run_forward(dict(d, x=d["x"][:64].contiguous()), 64, 512, 768, 8, 2)
+    pad = torch.ones(65, dtype=torch.uint8, device="cuda")
+    pad[64] = 0
+    b, _ = run_forward(dict(d, pad_mask=pad), 65, 512, 768, 8, 2)
+    assert np.max(np.abs(a - b[:64])) <= 1e-3 * rms(a)
+    del inp64
+
+
+def test_caller_workspace_matches_library_workspace():
+    inp, d = small_case("ws", T=100, d=256, f=512, n_pad=5)
+    a, _ = run_forward(d, 100, 256, 512, 8, 2)
+    need = moe.workspace_bytes(100, 256, 512, 8, 2)
+    ws = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+    b, _ = run_forward(d, 100, 256, 512, 8, 2, workspace=ws, ws_bytes=need)
+    assert np.array_equal(a, b)
+
+
+def test_workspace_allocation_failure_reports_nomem(monkeypatch):
+    inp, d = small_case("nomem", T=8, d=256, f=512)
+    moe.release_workspace()
+    monkeypatch.setenv("MOE_TEST_FAIL_ALLOC", "1")
+    out = torch.full((8, 256), 5.0, device="cuda")
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_forward(d["x"], d["router_w"], d["w_gate"], d["w_up"], d["w_down"], d["scales"], None, out,
+                        8, 256, 512, 8, 2)
+    assert ei.value.status == moe.MOE_ERR_NOMEM
+    torch.cuda.synchronize()
+    assert bool((out == 5.0).all())
+    monkeypatch.delenv("MOE_TEST_FAIL_ALLOC")
+    moe.moe_forward(d["x"], d["router_w"], d["w_gate"], d["w_up"], d["w_down"], d["scales"], None, out,
+                    8, 256, 512, 8, 2)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
