@@ -26,7 +26,7 @@
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE memory owned by the caller, row-major, and must
  *     stay valid until the work enqueued on `stream` completes. Pointers to vector data
- *     must be 16-byte aligned (x, weights, scales, out, h, y). The library never frees
+ *     must be 16-byte aligned (x, router_w, weights, scales, out, h, y). The library never frees
  *     or retains a caller pointer beyond the call.
  *   - `stream` is a hipStream_t (NULL = the default stream). All work is enqueued
  *     asynchronously; no entry point synchronises the host with the device, except the
@@ -123,7 +123,7 @@ int moe_gate_up(const void* x, const int32_t* perm, const int32_t* offsets, cons
 /* Step 3, second half: y = h (q_down[e] * s_down[e]) for the rows of every expert segment,
    with the contraction over f cut into `splits` equal parts: y fp32 [splits][T*k][d] holds
    one partial sum per part (their sum, in part order, is the result). splits must divide
-   f / 64. moe_down_splits() gives the count moe_forward uses for a shape. */
+   f / 128. moe_down_splits() gives the count moe_forward uses for a shape. */
 int moe_down(const void* h, const int32_t* offsets, const int8_t* w_down, const void* scales,
              float* y, int splits, int T, int d, int f, int E, int k, void* stream);
 int moe_down_splits(int T, int d, int f, int E, int k);

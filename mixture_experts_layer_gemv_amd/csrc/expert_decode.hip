@@ -4,43 +4,38 @@
 // GeLU expert gelu(linear(x)) * linear_v(x) -> linear_1; "Quantized weights": int8
 // weights dequantised as q * s, one scale per output channel.)
 //
-// Work split: one wavefront per workgroup owns a 128-column slab of one expert's
-// matrix (gate and up together for the first kernel) and runs down the whole
-// contraction (or one of `splits` parts of it for the down projection). Lane l takes the
-// 8 adjacent columns n0 + 8 (l % 16) .. + 7 and, per 32-deep step, the rows
-// k0 + 8 (l / 16) .. + 7: eight 8-byte loads per matrix, so each row segment a
-// wavefront touches is one full 128-byte line. Byte j of those eight rows is exactly
-// the B operand of one 16x16x32 MFMA (column j of the lane's 8 columns); the matching A
-// operand (8 bf16/fp16 activations of the same k-group) is one 16-byte load. The k
-// order inside an MFMA is the same permutation for A and B, so it does not change D.
-// The int8 -> bf16 / fp16 conversion is exact (one sign-extending byte convert plus
-// half a pack per element); scales are applied in fp32 after the contraction.
-// Loads for step s + 1 are issued before the MFMAs of step s (two register stages).
+// Work split: one wavefront owns a 128-column slab of one matrix of one touched expert
+// and runs down the whole contraction (or one of `splits` parts of it for the down
+// projection). For gate/up a workgroup holds two wavefronts, one per matrix, on the same
+// slab; they meet in LDS for the GeGLU epilogue. Lane l takes the 8 adjacent columns
+// n0 + 8 (l % 16) .. + 7 and, per 32-deep step, the rows k0 + 8 (l / 16) .. + 7: eight
+// 8-byte loads, so each row segment a wavefront touches is one full 128-byte line. Byte
+// j of those eight rows is exactly the B operand of one 16x16x32 MFMA (column j of the
+// lane's 8 columns); the matching A operand (8 bf16/fp16 activations of the same
+// k-group) is one 16-byte load. The k order inside an MFMA is the same permutation for A
+// and B, so it does not change D. The int8 -> bf16 / fp16 conversion is exact (one
+// sign-extending byte convert plus half a pack per element); scales are applied in fp32
+// after the contraction. Loads run kStages steps ahead of the MFMAs (register ring).
 //
-// Rows: an expert's segment of the dispatch has M rows (M <= T); a pass covers 32 of
-// them as two 16-row MFMA tiles (the second is skipped when the pass has <= 16 rows),
-// and segments longer than 32 rows take further passes over the weights.
+// Rows: an expert's segment of the dispatch has M rows (M <= T). A pass covers MT
+// 16-row MFMA tiles (MT = 1 when T <= 16, else 2);
+// longer segments take further passes over the weights.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace moe {
 
 namespace {
-constexpr int kSlab = 128;  // columns per wavefront
-constexpr int kStep = 32;   // contraction rows per MFMA step
+constexpr int kSlab = 128;   // columns per wavefront
+constexpr int kStep = 32;    // contraction rows per MFMA step
+constexpr int kStages = 4;   // steps of loads in flight per wavefront
+// Cache policy of the weight loads: non-temporal (each weight byte is read once).
+constexpr int kWeightLoadPolicy = 2;
+// Buffer resource word 3 for raw byte buffers on gfx9-family parts.
+constexpr int kBufferFlags = 0x00020000;
 }  // namespace
 
-// A operand: 8 consecutive activations (16 bytes) of one row; zero for rows past M.
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-
-__device__ __forceinline__ void load_rows8(uint32_t (&w)[8][2], const int8_t* p, size_t ld) {
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    u32x2 v = *reinterpret_cast<const u32x2*>(p + (size_t)r * ld);
-    w[r][0] = v.x;
-    w[r][1] = v.y;
-  }
-}
 
 template <int J, typename V>
 __device__ __forceinline__ V col_operand(const uint32_t (&w)[8][2]) {
@@ -53,111 +48,143 @@ __device__ __forceinline__ V col_operand(const uint32_t (&w)[8][2]) {
     return rows_to_f16<J & 3>(s);
 }
 
+// acc[mt][j] += A rows (tile mt) x column j of the lane's 8, over `steps` 32-deep steps.
+// wr: buffer resource of this expert's matrix; voff: byte offset of this lane's first
+// weight (row 8 kg, column n0); row r of step s is at voff + (32 s + r) * ld, with the
+// uniform part in the scalar offset, so all eight row loads share one address register.
+// a[mt]: this lane's first activation of tile mt (row cl of the tile, k 8 kg). Rows past
+// the segment end point at a live row: MFMA rows are independent, so their results are
+// simply not stored. steps must be a multiple of kStages; the steady-state loop has no
+// branches, so the loads of the next kStages - 1 steps stay in flight across the MFMAs.
+template <typename Frag, int MT>
+__device__ __forceinline__ void stream_slab(__amdgpu_buffer_rsrc_t wr, uint32_t voff, uint32_t ld, int steps,
+                                            const uint16_t* const (&a)[MT], f32x4 (&acc)[MT][8]) {
+  uint32_t b[kStages][8][2];
+  u32x4 av[kStages][MT];
+  auto load = [&](int s, int step) {
+    const uint32_t base = (uint32_t)step * kStep * ld;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      auto v = __builtin_amdgcn_raw_buffer_load_b64(wr, voff, base + r * ld, kWeightLoadPolicy);
+      b[s][r][0] = v[0];
+      b[s][r][1] = v[1];
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) av[s][mt] = load16(a[mt] + step * kStep);
+  };
+  auto compute = [&](int s) {
+    Frag af[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) af[mt] = __builtin_bit_cast(Frag, av[s][mt]);
+#define MOE_DEC_COL(J)                                                          \
+  {                                                                             \
+    Frag bfr = col_operand<J, Frag>(b[s]);                                      \
+    _Pragma("unroll") for (int mt = 0; mt < MT; ++mt)                           \
+        acc[mt][J] = Mfma<Frag>::run(af[mt], bfr, acc[mt][J]);                  \
+  }
+    MOE_DEC_COL(0) MOE_DEC_COL(1) MOE_DEC_COL(2) MOE_DEC_COL(3)
+    MOE_DEC_COL(4) MOE_DEC_COL(5) MOE_DEC_COL(6) MOE_DEC_COL(7)
+#undef MOE_DEC_COL
+  };
+
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) load(s, s);
+  int st = 0;
+  for (; st < steps - kStages; st += kStages) {
+#pragma unroll
+    for (int s = 0; s < kStages; ++s) {
+      load((s + kStages - 1) % kStages, st + s + kStages - 1);
+      compute(s);
+    }
+  }
+  load(kStages - 1, st + kStages - 1);  // the last step
+#pragma unroll
+  for (int s = 0; s < kStages; ++s) compute(s);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const int8_t* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(base), (short)0, (int)bytes, kBufferFlags);
+}
+
+__device__ __forceinline__ void load_scales8(const uint16_t* p, float (&s)[8]) {
+  u32x4 v = load16(p);
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s[j] = bf16_bits_to_float((w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+}
+
 // ------------------------------------------------------------------------------------
 // gate/up + GeGLU: H[row0 + m][n] = fp16(gelu_tanh(s_g[n] * G[m][n]) * (s_u[n] * U[m][n]))
-// grid (f / 128, E), block 64.
-__global__ __launch_bounds__(64) void gate_up_decode_kernel(
+// grid (f / 128, E), block 128: wavefront 0 = gate, wavefront 1 = up.
+template <int MT>
+__global__ __launch_bounds__(128) void gate_up_decode_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, const int8_t* __restrict__ w_gate,
     const int8_t* __restrict__ w_up, const uint16_t* __restrict__ scales, _Float16* __restrict__ H,
     int d, int f) {
+  __shared__ float s_up[MT * 16][kSlab + 4];  // s_u * U of the pass, [row][slab column]
   const int e = blockIdx.y;
   const int row0 = offsets[e];
   const int M = offsets[e + 1] - row0;
   if (M <= 0) return;
-  const int lane = threadIdx.x, kg = lane >> 4, cl = lane & 15;
-  const int n0 = blockIdx.x * kSlab + 8 * cl;
-  const size_t ld = (size_t)f;
-  const int8_t* pg = w_gate + (size_t)e * d * f + (size_t)(8 * kg) * ld + n0;
-  const int8_t* pu = w_up + (size_t)e * d * f + (size_t)(8 * kg) * ld + n0;
-  const uint16_t* sc = scales + (size_t)e * (2 * (size_t)f + d);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, kg = lane >> 4, cl = lane & 15;
+  const int nl = 8 * cl;  // first of the lane's 8 columns within the slab
+  const int n0 = blockIdx.x * kSlab + nl;
+  const __amdgpu_buffer_rsrc_t wr = weight_rsrc((wave == 0 ? w_gate : w_up) + (size_t)e * d * f, (size_t)d * f);
+  const uint32_t voff = (uint32_t)(8 * kg) * (uint32_t)f + (uint32_t)n0;
+  float s8[8];
+  load_scales8(scales + (size_t)e * (2 * (size_t)f + d) + (wave == 0 ? 0 : f) + n0, s8);
 
-  for (int pb = 0; pb < M; pb += 32) {
-    const bool two = (M - pb) > 16;
-    // A rows of this lane: m = pb + cl (tile 0) and pb + 16 + cl (tile 1).
-    const uint16_t* xa[2];
-    bool va[2];
+  for (int pb = 0; pb < M; pb += 16 * MT) {
+    const uint16_t* a[MT];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      int m = pb + 16 * mt + cl;
-      va[mt] = m < M;
-      int tok = va[mt] ? perm[row0 + m] : 0;
-      xa[mt] = x + (size_t)tok * d + 8 * kg;
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = min(pb + 16 * mt + cl, M - 1);
+      a[mt] = x + (size_t)perm[row0 + m] * d + 8 * kg;
     }
-    f32x4 accg[2][8], accu[2][8];
+    f32x4 acc[MT][8];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) accg[mt][j] = accu[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 8; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    stream_slab<bf16x8, MT>(wr, voff, (uint32_t)f, d / kStep, a, acc);
 
-    uint32_t bg[2][8][2], bu[2][8][2];
-    u32x4 av[2][2];
-    auto load_stage = [&](int s, int kk) {
-      load_rows8(bg[s], pg + (size_t)kk * ld, ld);
-      load_rows8(bu[s], pu + (size_t)kk * ld, ld);
+    // lane holds rows 16 mt + 4 kg + i of the pass, columns nl .. nl + 7 of the slab
+    if (wave == 1) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) av[s][mt] = va[mt] ? load16(xa[mt] + kk) : zero_u32x4();
-    };
-    auto compute_stage = [&](int s) {
-      bf16x8 a0 = __builtin_bit_cast(bf16x8, av[s][0]);
-      bf16x8 a1 = __builtin_bit_cast(bf16x8, av[s][1]);
-#define MOE_GU_COL(J)                                                   \
-  {                                                                     \
-    bf16x8 b = col_operand<J, bf16x8>(bg[s]);                           \
-    accg[0][J] = Mfma<bf16x8>::run(a0, b, accg[0][J]);                  \
-    if (two) accg[1][J] = Mfma<bf16x8>::run(a1, b, accg[1][J]);         \
-    bf16x8 c = col_operand<J, bf16x8>(bu[s]);                           \
-    accu[0][J] = Mfma<bf16x8>::run(a0, c, accu[0][J]);                  \
-    if (two) accu[1][J] = Mfma<bf16x8>::run(a1, c, accu[1][J]);         \
-  }
-      MOE_GU_COL(0) MOE_GU_COL(1) MOE_GU_COL(2) MOE_GU_COL(3)
-      MOE_GU_COL(4) MOE_GU_COL(5) MOE_GU_COL(6) MOE_GU_COL(7)
-#undef MOE_GU_COL
-    };
-
-    load_stage(0, 0);
-    for (int kk = 0; kk < d; kk += 2 * kStep) {
-      load_stage(1, kk + kStep);
-      compute_stage(0);
-      if (kk + 2 * kStep < d) load_stage(0, kk + 2 * kStep);
-      compute_stage(1);
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) s_up[16 * mt + 4 * kg + i][nl + j] = acc[mt][j][i] * s8[j];
     }
-
-    // Epilogue: lane holds rows 4 kg + i of each tile, columns n0 .. n0 + 7.
-    float sg[8], su[8];
-    {
-      u32x4 g4 = load16(sc + n0), u4 = load16(sc + f + n0);
-      uint32_t gw[4] = {g4.x, g4.y, g4.z, g4.w}, uw[4] = {u4.x, u4.y, u4.z, u4.w};
+    __syncthreads();
+    if (wave == 0) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        sg[j] = bf16_bits_to_float((gw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-        su[j] = bf16_bits_to_float((uw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-      }
-    }
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+        for (int i = 0; i < 4; ++i) {
+          const int m = pb + 16 * mt + 4 * kg + i;
+          if (m < M) {
+            const float* urow = s_up[16 * mt + 4 * kg + i] + nl;
+            uint32_t packed[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = pb + 16 * mt + 4 * kg + i;
-        if (m < M) {
-          uint32_t packed[4];
-#pragma unroll
-          for (int j = 0; j < 8; j += 2) {
-            float h0 = gelu_tanh(accg[mt][j][i] * sg[j]) * (accu[mt][j][i] * su[j]);
-            float h1 = gelu_tanh(accg[mt][j + 1][i] * sg[j + 1]) * (accu[mt][j + 1][i] * su[j + 1]);
-            packed[j >> 1] = pack_f16_rne(h0, h1);
+            for (int j = 0; j < 8; j += 2)
+              packed[j >> 1] = pack_f16_rne(gelu_tanh(acc[mt][j][i] * s8[j]) * urow[j],
+                                            gelu_tanh(acc[mt][j + 1][i] * s8[j + 1]) * urow[j + 1]);
+            u32x4 v = {packed[0], packed[1], packed[2], packed[3]};
+            *reinterpret_cast<u32x4*>(H + (size_t)(row0 + m) * f + n0) = v;
           }
-          u32x4 v = {packed[0], packed[1], packed[2], packed[3]};
-          *reinterpret_cast<u32x4*>(H + (size_t)(row0 + m) * f + n0) = v;
         }
-      }
     }
+    __syncthreads();  // s_up is rewritten by the next pass
   }
 }
 
 // ------------------------------------------------------------------------------------
 // down: Y[s][row0 + m][n] = s_d[n] * sum over k in part s of H[row0 + m][k] * q_d[k][n]
 // grid (d / 128, splits, E), block 64.
+template <int MT>
 __global__ __launch_bounds__(64) void down_decode_kernel(
     const _Float16* __restrict__ H, const int32_t* __restrict__ offsets,
     const int8_t* __restrict__ w_down, const uint16_t* __restrict__ scales, float* __restrict__ Y,
@@ -169,65 +196,28 @@ __global__ __launch_bounds__(64) void down_decode_kernel(
   const int kspan = f / gridDim.y, kbeg = part * kspan;
   const int lane = threadIdx.x, kg = lane >> 4, cl = lane & 15;
   const int n0 = blockIdx.x * kSlab + 8 * cl;
-  const size_t ld = (size_t)d;
-  const int8_t* pd = w_down + (size_t)e * f * d + (size_t)(kbeg + 8 * kg) * ld + n0;
-  const uint16_t* sc = scales + (size_t)e * (2 * (size_t)f + d) + 2 * (size_t)f;
+  const __amdgpu_buffer_rsrc_t wr = weight_rsrc(w_down + (size_t)e * f * d, (size_t)f * d);
+  const uint32_t voff = (uint32_t)(kbeg + 8 * kg) * (uint32_t)d + (uint32_t)n0;
+  float sd[8];
+  load_scales8(scales + (size_t)e * (2 * (size_t)f + d) + 2 * (size_t)f + n0, sd);
   float* Yp = Y + (size_t)part * rows_cap * d;
 
-  for (int pb = 0; pb < M; pb += 32) {
-    const bool two = (M - pb) > 16;
-    const _Float16* ha[2];
-    bool va[2];
+  for (int pb = 0; pb < M; pb += 16 * MT) {
+    const uint16_t* a[MT];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      int m = pb + 16 * mt + cl;
-      va[mt] = m < M;
-      ha[mt] = H + (size_t)(row0 + (va[mt] ? m : 0)) * f + kbeg + 8 * kg;
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = min(pb + 16 * mt + cl, M - 1);
+      a[mt] = reinterpret_cast<const uint16_t*>(H) + (size_t)(row0 + m) * f + kbeg + 8 * kg;
     }
-    f32x4 acc[2][8];
+    f32x4 acc[MT][8];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    stream_slab<f16x8, MT>(wr, voff, (uint32_t)d, kspan / kStep, a, acc);
 
-    uint32_t bd[2][8][2];
-    u32x4 av[2][2];
-    auto load_stage = [&](int s, int kk) {
-      load_rows8(bd[s], pd + (size_t)kk * ld, ld);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) av[s][mt] = va[mt] ? load16(ha[mt] + kk) : zero_u32x4();
-    };
-    auto compute_stage = [&](int s) {
-      f16x8 a0 = __builtin_bit_cast(f16x8, av[s][0]);
-      f16x8 a1 = __builtin_bit_cast(f16x8, av[s][1]);
-#define MOE_DN_COL(J)                                                 \
-  {                                                                   \
-    f16x8 b = col_operand<J, f16x8>(bd[s]);                           \
-    acc[0][J] = Mfma<f16x8>::run(a0, b, acc[0][J]);                   \
-    if (two) acc[1][J] = Mfma<f16x8>::run(a1, b, acc[1][J]);          \
-  }
-      MOE_DN_COL(0) MOE_DN_COL(1) MOE_DN_COL(2) MOE_DN_COL(3)
-      MOE_DN_COL(4) MOE_DN_COL(5) MOE_DN_COL(6) MOE_DN_COL(7)
-#undef MOE_DN_COL
-    };
-
-    load_stage(0, 0);
-    for (int kk = 0; kk < kspan; kk += 2 * kStep) {
-      load_stage(1, kk + kStep);
-      compute_stage(0);
-      if (kk + 2 * kStep < kspan) load_stage(0, kk + 2 * kStep);
-      compute_stage(1);
-    }
-
-    float sd[8];
-    {
-      u32x4 d4 = load16(sc + n0);
-      uint32_t dw[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sd[j] = bf16_bits_to_float((dw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-    }
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = pb + 16 * mt + 4 * kg + i;
@@ -239,23 +229,32 @@ __global__ __launch_bounds__(64) void down_decode_kernel(
           reinterpret_cast<f32x4*>(dst)[1] = hi;
         }
       }
-    }
   }
 }
 
 hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* perm, const int32_t* offsets,
                                  const int8_t* w_gate, const int8_t* w_up, const uint16_t* scales,
-                                 _Float16* H, int d, int f, int E, hipStream_t stream) {
-  hipLaunchKernelGGL(gate_up_decode_kernel, dim3(f / kSlab, E), dim3(64), 0, stream, x, perm,
-                     offsets, w_gate, w_up, scales, H, d, f);
+                                 _Float16* H, int T, int d, int f, int E, hipStream_t stream) {
+  dim3 grid(f / kSlab, E), block(128);
+  if (T <= 16)
+    hipLaunchKernelGGL(gate_up_decode_kernel<1>, grid, block, 0, stream, x, perm, offsets, w_gate, w_up,
+                       scales, H, d, f);
+  else
+    hipLaunchKernelGGL(gate_up_decode_kernel<2>, grid, block, 0, stream, x, perm, offsets, w_gate, w_up,
+                       scales, H, d, f);
   return hipGetLastError();
 }
 
 hipError_t launch_down_decode(const _Float16* H, const int32_t* offsets, const int8_t* w_down,
-                              const uint16_t* scales, float* Y, int splits, int rows_cap, int d,
-                              int f, int E, hipStream_t stream) {
-  hipLaunchKernelGGL(down_decode_kernel, dim3(d / kSlab, splits, E), dim3(64), 0, stream, H,
-                     offsets, w_down, scales, Y, d, f, rows_cap);
+                              const uint16_t* scales, float* Y, int splits, int rows_cap, int T,
+                              int d, int f, int E, hipStream_t stream) {
+  dim3 grid(d / kSlab, splits, E), block(64);
+  if (T <= 16)
+    hipLaunchKernelGGL(down_decode_kernel<1>, grid, block, 0, stream, H, offsets, w_down, scales, Y, d,
+                       f, rows_cap);
+  else
+    hipLaunchKernelGGL(down_decode_kernel<2>, grid, block, 0, stream, H, offsets, w_down, scales, Y, d,
+                       f, rows_cap);
   return hipGetLastError();
 }
 

@@ -4,21 +4,22 @@
 // dequantised as q * s with one scale per output channel, compute in bf16.)
 //
 // One workgroup (256 threads, 4 wavefronts in a 2 x 2 arrangement) computes a
-// 128-row x 256-column tile of one expert: for the gate/up kernel 128 columns of gate
+// 256-row x 256-column tile of one expert: for the gate/up kernel 128 columns of gate
 // and the same 128 of up (so the GeGLU is applied in registers), for the down kernel
-// 256 columns of the down projection. The contraction runs in 64-deep slices:
+// 256 columns of the down projection. Each wavefront owns 128 rows x 128 columns as
+// 4 x 4 tiles of the 32x32x16 MFMA (256 fp32 accumulators per lane), which keeps the LDS
+// bytes read per MFMA low. The contraction runs in 64-deep slices:
 //   * the next slice's activations (16 B per load) and int8 weights (one dword of 4
-//     columns from each of 8 rows per thread and half-tile) are loaded into registers
-//     while the MFMAs of the current slice run;
+//     columns from each of 8 rows per thread and half-tile, through buffer loads whose
+//     row offset is a scalar) are loaded into registers while the current slice's MFMAs
+//     run, then written into the other of two LDS buffers (one barrier per slice);
 //   * the weights are converted int8 -> bf16 (gate/up) or fp16 (down) once per
-//     workgroup, on the way into LDS, and stored transposed ([column][k]), so every
-//     MFMA operand is one 16-byte LDS read; column 4 c + q of a 64-column group goes to
-//     LDS row 16 q + c, which keeps those reads conflict-free and gives each lane 4
-//     adjacent output columns in the epilogue;
-//   * each wavefront owns 64 rows x 128 columns: 4 x 8 MFMA tiles of 16x16x32.
+//     workgroup, on the way into LDS, and stored transposed ([column][k]), so every MFMA
+//     operand is one 16-byte LDS read; column 2 c + q of a 64-column group goes to LDS
+//     row 32 q + c, which gives each lane 2 adjacent output columns in the epilogue.
 // Rows are gathered through the dispatch permutation (gate/up) or read in segment order
 // (down). Tiles are assigned on the device: blockIdx.x enumerates the m-tiles of all
-// expert segments in expert order (read from offsets), surplus slots exit at once.
+// expert segments in expert order (read from offsets); surplus slots exit at once.
 // Scales, GeLU and the fp16 rounding of h are applied in fp32 after the contraction.
 #include "device_common.h"
 #include "kernels.h"
@@ -26,20 +27,44 @@
 namespace moe {
 
 namespace {
-constexpr int BM = 128;        // rows per workgroup tile
-constexpr int BK = 64;         // contraction depth per slice
-constexpr int HALF = 128;      // columns per weight half-tile
-constexpr int LDS_LD = BK + 8; // 16-bit elements per LDS row (16-byte pad)
+constexpr int BM = 256;         // rows per workgroup tile
+constexpr int BK = 64;          // contraction depth per slice
+constexpr int HALF = 128;       // columns per weight half-tile
+constexpr int LDS_LD = BK + 8;  // 16-bit elements per LDS row (16-byte pad)
 constexpr int kThreads = 256;
+constexpr int A_ELEMS = BM * LDS_LD;
+constexpr int B_ELEMS = 2 * HALF * LDS_LD;
+constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;  // 36864 x 2 B = 72 KiB per buffer
+constexpr int kBufferFlags = 0x00020000;
 }  // namespace
 
-// (expert, m-tile) of m-slot `slot`, or false when the slot is surplus.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <typename T>
+struct Mfma32;
+// D(32x32 fp32) += A(32x16) * B(16x32). Lane l supplies A row (l % 32) and B column
+// (l % 32) with the 8 k-values of k-group (l / 32); D element i of lane l is row
+// 8 (i / 4) + 4 (l / 32) + (i % 4), column l % 32.
+template <>
+struct Mfma32<bf16x8> {
+  static __device__ __forceinline__ f32x16 run(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Mfma32<f16x8> {
+  static __device__ __forceinline__ f32x16 run(f16x8 a, f16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+// (expert, first row, rows) of m-slot `slot`, or false when the slot is surplus.
 __device__ __forceinline__ bool find_tile(const int32_t* offsets, int E, int slot, int& e, int& row0,
                                           int& rows) {
   int s = slot;
   for (int ee = 0; ee < E; ++ee) {
-    int M = offsets[ee + 1] - offsets[ee];
-    int nt = (M + BM - 1) / BM;
+    const int M = offsets[ee + 1] - offsets[ee];
+    const int nt = (M + BM - 1) / BM;
     if (s < nt) {
       e = ee;
       row0 = offsets[ee] + s * BM;
@@ -53,7 +78,6 @@ __device__ __forceinline__ bool find_tile(const int32_t* offsets, int E, int slo
 
 template <bool kGateUp>
 struct PrefillTraits;
-
 template <>
 struct PrefillTraits<true> {
   using Frag = bf16x8;
@@ -65,17 +89,17 @@ struct PrefillTraits<false> {
   static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_f16(a, b); }
 };
 
-// Writes the 4 columns x 8 rows held by a thread (dword per row) into LDS, transposed and
-// converted: column q of the thread's 4 goes to LDS row `row_base + 16 q`.
-template <bool kGateUp, int Q>
-__device__ __forceinline__ void store_col(uint16_t* sB, int row_base, int koff, const uint32_t (&w)[8]) {
+// Column JJ (0..3) of the thread's 4 columns over its 8 rows, converted, as one 16-byte
+// LDS write at row `row` (k offset koff).
+template <bool kGateUp, int JJ>
+__device__ __forceinline__ void store_col(uint16_t* sB, int row, int koff, const uint32_t (&w)[8]) {
   using P = PrefillTraits<kGateUp>;
   u32x4 v;
-  v.x = P::pack(sbyte<Q>(w[0]), sbyte<Q>(w[1]));
-  v.y = P::pack(sbyte<Q>(w[2]), sbyte<Q>(w[3]));
-  v.z = P::pack(sbyte<Q>(w[4]), sbyte<Q>(w[5]));
-  v.w = P::pack(sbyte<Q>(w[6]), sbyte<Q>(w[7]));
-  *reinterpret_cast<u32x4*>(sB + (size_t)(row_base + 16 * Q) * LDS_LD + koff) = v;
+  v.x = P::pack(sbyte<JJ>(w[0]), sbyte<JJ>(w[1]));
+  v.y = P::pack(sbyte<JJ>(w[2]), sbyte<JJ>(w[3]));
+  v.z = P::pack(sbyte<JJ>(w[4]), sbyte<JJ>(w[5]));
+  v.w = P::pack(sbyte<JJ>(w[6]), sbyte<JJ>(w[7]));
+  *reinterpret_cast<u32x4*>(sB + (size_t)row * LDS_LD + koff) = v;
 }
 
 // kGateUp: A = x rows gathered by perm (bf16), B halves = gate / up at columns n0..n0+127,
@@ -83,153 +107,159 @@ __device__ __forceinline__ void store_col(uint16_t* sB, int row_base, int koff, 
 // !kGateUp: A = H rows (fp16), B halves = down columns n0..n0+127 and n0+128..n0+255,
 //          output Y fp32 (part blockIdx.z of the contraction) = s_d y.
 template <bool kGateUp>
-__global__ __launch_bounds__(kThreads, 2) void expert_prefill_kernel(
+__global__ __launch_bounds__(kThreads, 1) void expert_prefill_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, const int8_t* __restrict__ B0,
     const int8_t* __restrict__ B1, const uint16_t* __restrict__ scales, void* __restrict__ out,
     int d, int f, int E, int rows_cap) {
   using Frag = typename PrefillTraits<kGateUp>::Frag;
-  __shared__ __attribute__((aligned(16))) uint16_t sA[BM * LDS_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2 * HALF * LDS_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE_ELEMS];
 
   int e, row0, rows;
   if (!find_tile(offsets, E, blockIdx.x, e, row0, rows)) return;
 
-  const int K = kGateUp ? d : f;             // contraction length
-  const int N = kGateUp ? f : d;             // output columns (per matrix)
+  const int K = kGateUp ? d : f;  // contraction length
+  const int N = kGateUp ? f : d;  // columns of each weight matrix
   const int kspan = K / gridDim.z, kbeg = blockIdx.z * kspan;
   const int n0 = blockIdx.y * (kGateUp ? HALF : 2 * HALF);
-  const size_t ldb = (size_t)N;
-  const size_t ebase = (size_t)e * d * f;
+  const uint32_t ldb = (uint32_t)N;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- per-thread global load descriptors
-  // A: rows tid / 8 + 32 i (i = 0..3), 16-byte chunk tid % 8 of the slice
-  const uint16_t* arow[4];
-  bool avalid[4];
+  // ---- global -> register loads of one slice
+  // A: rows tid / 8 + 32 i (i = 0..7), 16-byte chunk tid % 8 of the slice
+  const uint16_t* arow[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int m = tid / 8 + 32 * i;
-    avalid[i] = m < rows;
-    int r = row0 + (avalid[i] ? m : 0);
-    size_t src_row = kGateUp ? (size_t)perm[r] : (size_t)r;
+  for (int i = 0; i < 8; ++i) {
+    const int m = min(tid / 8 + 32 * i, rows - 1);  // rows past the tile end repeat a live row
+    const size_t src_row = kGateUp ? (size_t)perm[row0 + m] : (size_t)(row0 + m);
     arow[i] = A + src_row * K + kbeg + 8 * (tid % 8);
   }
   // B: columns 4 cg .. 4 cg + 3 of each half, rows 8 kg .. 8 kg + 7 of the slice
   const int cg = tid % 32, kg = tid / 32;
-  const int8_t* bsrc[2];
-  bsrc[0] = B0 + ebase + (size_t)(kbeg + 8 * kg) * ldb + n0 + 4 * cg;
-  bsrc[1] = (kGateUp ? B1 + ebase + n0 : B0 + ebase + n0 + HALF) + (size_t)(kbeg + 8 * kg) * ldb + 4 * cg;
-  // LDS row of column 4 c + q (c = cg % 16) of 64-column group cg / 16, half h:
-  //   h * 128 + (cg / 16) * 64 + 16 q + cg % 16
-  const int brow = (cg / 16) * 64 + (cg % 16);
+  const size_t ebytes = (size_t)d * f;
+  const int8_t* hbase0 = B0 + (size_t)e * ebytes;
+  const int8_t* hbase1 = kGateUp ? B1 + (size_t)e * ebytes : hbase0;
+  const __amdgpu_buffer_rsrc_t br0 =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(hbase0), (short)0, (int)ebytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t br1 =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(hbase1), (short)0, (int)ebytes, kBufferFlags);
+  const uint32_t bvoff0 = (uint32_t)(8 * kg) * ldb + (uint32_t)(n0 + 4 * cg);
+  const uint32_t bvoff1 = bvoff0 + (kGateUp ? 0u : (uint32_t)HALF);
+  // LDS row of the thread's column jj: half h, group cg / 16, column 4 (cg % 16) + jj
+  //   -> h * 128 + (cg / 16) * 64 + 32 (jj % 2) + 2 (cg % 16) + jj / 2
+  const int brow = (cg / 16) * 64 + 2 * (cg % 16);
 
-  u32x4 ra[4];
+  u32x4 ra[8];
   uint32_t rb[2][8];
   auto gload = [&](int kk) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = avalid[i] ? *reinterpret_cast<const u32x4*>(arow[i] + kk) : zero_u32x4();
+    for (int i = 0; i < 8; ++i) ra[i] = *reinterpret_cast<const u32x4*>(arow[i] + kk);
+    const uint32_t sbase = (uint32_t)(kbeg + kk) * ldb;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int r = 0; r < 8; ++r) rb[h][r] = *reinterpret_cast<const uint32_t*>(bsrc[h] + (size_t)(kk + r) * ldb);
+    for (int r = 0; r < 8; ++r) {
+      rb[0][r] = __builtin_amdgcn_raw_buffer_load_b32(br0, bvoff0, sbase + r * ldb, 0);
+      rb[1][r] = __builtin_amdgcn_raw_buffer_load_b32(br1, bvoff1, sbase + r * ldb, 0);
+    }
   };
-  auto lds_store = [&]() {
+  auto lds_store = [&](uint16_t* st) {
+    uint16_t* sA = st;
+    uint16_t* sB = st + A_ELEMS;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
       *reinterpret_cast<u32x4*>(sA + (size_t)(tid / 8 + 32 * i) * LDS_LD + 8 * (tid % 8)) = ra[i];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      store_col<kGateUp, 0>(sB, h * HALF + brow, 8 * kg, rb[h]);
-      store_col<kGateUp, 1>(sB, h * HALF + brow, 8 * kg, rb[h]);
-      store_col<kGateUp, 2>(sB, h * HALF + brow, 8 * kg, rb[h]);
-      store_col<kGateUp, 3>(sB, h * HALF + brow, 8 * kg, rb[h]);
+      store_col<kGateUp, 0>(sB, h * HALF + brow + 0, 8 * kg, rb[h]);
+      store_col<kGateUp, 1>(sB, h * HALF + brow + 32, 8 * kg, rb[h]);
+      store_col<kGateUp, 2>(sB, h * HALF + brow + 1, 8 * kg, rb[h]);
+      store_col<kGateUp, 3>(sB, h * HALF + brow + 33, 8 * kg, rb[h]);
     }
   };
 
-  // ---- wavefront tile: rows wm * 64 + 16 mt + (lane % 16); B tiles nt = 4 grp + q
-  //   gate/up: grp 0 = gate, grp 1 = up, both at columns wn * 64 .. + 63 of the half
-  //   down:    grp 0/1 = columns wn * 128 + grp * 64 .. + 63
-  int bro[2];
+  // ---- wavefront tile: rows wm * 128 + 32 mt + (lane % 32); B tiles nt: LDS rows
+  //   gate/up: (nt / 2) * 128 + wn * 64 + 32 (nt % 2) + (lane % 32)   (nt 0,1 gate; 2,3 up)
+  //   down:    wn * 128 + (nt / 2) * 64 + 32 (nt % 2) + (lane % 32)
+  int bro[4];
 #pragma unroll
-  for (int g = 0; g < 2; ++g)
-    bro[g] = kGateUp ? g * HALF + wn * 64 : wn * HALF + g * 64;
-  const int kq = 8 * (lane >> 4), lr = lane & 15;
+  for (int nt = 0; nt < 4; ++nt)
+    bro[nt] = (kGateUp ? (nt >> 1) * HALF + wn * 64 : wn * HALF + (nt >> 1) * 64) + 32 * (nt & 1) + (lane & 31);
+  const int kq = 8 * (lane >> 5);
+  const int arl = wm * 128 + (lane & 31);
 
-  f32x4 acc[4][8];
+  f32x16 acc[4][4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  gload(0);
-  for (int kk = 0; kk < kspan; kk += BK) {
-    __syncthreads();  // previous slice's LDS reads are done
-    lds_store();
-    __syncthreads();
-    if (kk + BK < kspan) gload(kk + BK);
+    for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-    for (int ks = 0; ks < BK; ks += 32) {
+      for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.0f;
+
+  const int nslices = kspan / BK;
+  gload(0);
+  lds_store(lds);
+  __syncthreads();
+  for (int it = 0; it < nslices; ++it) {
+    const uint16_t* cur = lds + (it & 1) * STAGE_ELEMS;
+    if (it + 1 < nslices) gload((it + 1) * BK);
+    const uint16_t* sA = cur;
+    const uint16_t* sB = cur + A_ELEMS;
+#pragma unroll
+    for (int ks = 0; ks < BK; ks += 16) {
       Frag af[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        af[mt] = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(
-                                              sA + (size_t)(wm * 64 + 16 * mt + lr) * LDS_LD + ks + kq));
+        af[mt] = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(sA + (size_t)(arl + 32 * mt) * LDS_LD + ks + kq));
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const int row = bro[nt >> 2] + 16 * (nt & 3) + lr;
-        Frag bfr = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(sB + (size_t)row * LDS_LD + ks + kq));
+      for (int nt = 0; nt < 4; ++nt) {
+        const Frag bfr = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(sB + (size_t)bro[nt] * LDS_LD + ks + kq));
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = Mfma<Frag>::run(af[mt], bfr, acc[mt][nt]);
+        for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = Mfma32<Frag>::run(af[mt], bfr, acc[mt][nt]);
       }
     }
+    if (it + 1 < nslices) lds_store(lds + ((it + 1) & 1) * STAGE_ELEMS);
+    __syncthreads();
   }
 
-  // ---- epilogue: lane holds rows wm*64 + 16 mt + 4 (lane/16) + i and, per group,
-  //      the 4 adjacent columns 4 (lane % 16) + q, q = 0..3
+  // ---- epilogue: lane holds, per tile (mt, nt), rows wm*128 + 32 mt + 8 (i/4) + 4 (lane/32)
+  //      + i % 4 (i = 0..15) of column 2 (lane % 32) + (nt % 2) of its 64-column group
   const uint16_t* sc = scales + (size_t)e * (2 * (size_t)f + d);
-  const int rq = 4 * (lane >> 4);
+  const int c2 = 2 * (lane & 31);
+  const int rq = 4 * (lane >> 5);
   if constexpr (kGateUp) {
-    const int n = n0 + wn * 64 + 4 * lr;
-    float sg[4], su[4];
-    u32x2 g2 = *reinterpret_cast<const u32x2*>(sc + n), u2 = *reinterpret_cast<const u32x2*>(sc + f + n);
-    sg[0] = bf16_bits_to_float(g2.x & 0xFFFFu), sg[1] = bf16_bits_to_float(g2.x >> 16);
-    sg[2] = bf16_bits_to_float(g2.y & 0xFFFFu), sg[3] = bf16_bits_to_float(g2.y >> 16);
-    su[0] = bf16_bits_to_float(u2.x & 0xFFFFu), su[1] = bf16_bits_to_float(u2.x >> 16);
-    su[2] = bf16_bits_to_float(u2.y & 0xFFFFu), su[3] = bf16_bits_to_float(u2.y >> 16);
+    const int n = n0 + wn * 64 + c2;
+    const uint32_t g2 = *reinterpret_cast<const uint32_t*>(sc + n);
+    const uint32_t u2 = *reinterpret_cast<const uint32_t*>(sc + f + n);
+    const float sg0 = bf16_bits_to_float(g2 & 0xFFFFu), sg1 = bf16_bits_to_float(g2 >> 16);
+    const float su0 = bf16_bits_to_float(u2 & 0xFFFFu), su1 = bf16_bits_to_float(u2 >> 16);
     _Float16* H = reinterpret_cast<_Float16*>(out);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = wm * 64 + 16 * mt + rq + i;
+      for (int i = 0; i < 16; ++i) {
+        const int m = wm * 128 + 32 * mt + 8 * (i >> 2) + rq + (i & 3);
         if (m < rows) {
-          float h[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) h[q] = gelu_tanh(acc[mt][q][i] * sg[q]) * (acc[mt][4 + q][i] * su[q]);
-          u32x2 v = {pack_f16_rne(h[0], h[1]), pack_f16_rne(h[2], h[3])};
-          *reinterpret_cast<u32x2*>(H + (size_t)(row0 + m) * f + n) = v;
+          const float h0 = gelu_tanh(acc[mt][0][i] * sg0) * (acc[mt][2][i] * su0);
+          const float h1 = gelu_tanh(acc[mt][1][i] * sg1) * (acc[mt][3][i] * su1);
+          *reinterpret_cast<uint32_t*>(H + (size_t)(row0 + m) * f + n) = pack_f16_rne(h0, h1);
         }
       }
   } else {
     float* Y = reinterpret_cast<float*>(out) + (size_t)blockIdx.z * rows_cap * d;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      const int n = n0 + wn * HALF + g * 64 + 4 * lr;
-      u32x2 s2 = *reinterpret_cast<const u32x2*>(sc + 2 * (size_t)f + n);
-      float sd[4] = {bf16_bits_to_float(s2.x & 0xFFFFu), bf16_bits_to_float(s2.x >> 16),
-                     bf16_bits_to_float(s2.y & 0xFFFFu), bf16_bits_to_float(s2.y >> 16)};
+      const int n = n0 + wn * HALF + g * 64 + c2;
+      const uint32_t s2 = *reinterpret_cast<const uint32_t*>(sc + 2 * (size_t)f + n);
+      const float sd0 = bf16_bits_to_float(s2 & 0xFFFFu), sd1 = bf16_bits_to_float(s2 >> 16);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = wm * 64 + 16 * mt + rq + i;
+        for (int i = 0; i < 16; ++i) {
+          const int m = wm * 128 + 32 * mt + 8 * (i >> 2) + rq + (i & 3);
           if (m < rows) {
-            f32x4 v = {acc[mt][4 * g + 0][i] * sd[0], acc[mt][4 * g + 1][i] * sd[1],
-                       acc[mt][4 * g + 2][i] * sd[2], acc[mt][4 * g + 3][i] * sd[3]};
-            *reinterpret_cast<f32x4*>(Y + (size_t)(row0 + m) * d + n) = v;
+            u32x2 v = {__float_as_uint(acc[mt][2 * g][i] * sd0), __float_as_uint(acc[mt][2 * g + 1][i] * sd1)};
+            *reinterpret_cast<u32x2*>(Y + (size_t)(row0 + m) * d + n) = v;
           }
         }
     }

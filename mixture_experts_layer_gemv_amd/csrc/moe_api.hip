@@ -62,7 +62,7 @@ int down_splits(int T, int f) {
   int s = f / 4096;
   if (s < 1) s = 1;
   if (s > 8) s = 8;
-  while (s > 1 && (f / 64) % s != 0) s /= 2;
+  while (s > 1 && (f / 128) % s != 0) s /= 2;
   return s;
 }
 
@@ -137,7 +137,7 @@ int check_layer_args(const void* x, const float* router_w, const int8_t* w_gate,
                      int k) {
   MOE_TRY(check_shape(T, d, f, E, k));
   MOE_TRY(check_ptr(x, "x"));
-  MOE_TRY(check_ptr(router_w, "router_w", 4));
+  MOE_TRY(check_ptr(router_w, "router_w"));
   MOE_TRY(check_ptr(w_gate, "w_gate"));
   MOE_TRY(check_ptr(w_up, "w_up"));
   MOE_TRY(check_ptr(w_down, "w_down"));
@@ -151,8 +151,8 @@ int run_experts(const uint16_t* x, const int32_t* perm, const int32_t* offsets, 
                 float* y, int splits, int T, int d, int f, int E, int k, hipStream_t s) {
   const int rows_cap = T * k;
   if (T <= moe::kDecodeMaxT) {
-    MOE_HIP(moe::launch_gate_up_decode(x, perm, offsets, w_gate, w_up, scales, h, d, f, E, s), "gate_up");
-    MOE_HIP(moe::launch_down_decode(h, offsets, w_down, scales, y, splits, rows_cap, d, f, E, s), "down");
+    MOE_HIP(moe::launch_gate_up_decode(x, perm, offsets, w_gate, w_up, scales, h, T, d, f, E, s), "gate_up");
+    MOE_HIP(moe::launch_down_decode(h, offsets, w_down, scales, y, splits, rows_cap, T, d, f, E, s), "down");
   } else {
     MOE_HIP(moe::launch_gate_up_prefill(x, perm, offsets, w_gate, w_up, scales, h, rows_cap, d, f, E, s),
             "gate_up");
@@ -252,7 +252,7 @@ int moe_route(const void* x, const float* router_w, const float* router_bias, co
               int32_t* topk_ids, float* topk_w, int T, int d, int E, int k, void* stream) {
   MOE_TRY(check_shape(T, d, 256, E, k));
   MOE_TRY(check_ptr(x, "x"));
-  MOE_TRY(check_ptr(router_w, "router_w", 4));
+  MOE_TRY(check_ptr(router_w, "router_w"));
   MOE_TRY(check_ptr(topk_ids, "topk_ids", 4));
   MOE_TRY(check_ptr(topk_w, "topk_w", 4));
   if (T == 0) return MOE_OK;
@@ -293,7 +293,7 @@ int moe_gate_up(const void* x, const int32_t* perm, const int32_t* offsets, cons
   const auto* sc = static_cast<const uint16_t*>(scales);
   auto* hh = static_cast<_Float16*>(h);
   if (T <= moe::kDecodeMaxT)
-    MOE_HIP(moe::launch_gate_up_decode(xb, perm, offsets, w_gate, w_up, sc, hh, d, f, E, s), "gate_up");
+    MOE_HIP(moe::launch_gate_up_decode(xb, perm, offsets, w_gate, w_up, sc, hh, T, d, f, E, s), "gate_up");
   else
     MOE_HIP(moe::launch_gate_up_prefill(xb, perm, offsets, w_gate, w_up, sc, hh, T * k, d, f, E, s), "gate_up");
   return MOE_OK;
@@ -307,13 +307,13 @@ int moe_down(const void* h, const int32_t* offsets, const int8_t* w_down, const 
   MOE_TRY(check_ptr(w_down, "w_down"));
   MOE_TRY(check_ptr(scales, "scales"));
   MOE_TRY(check_ptr(y, "y"));
-  if (splits < 1 || (f / 64) % splits != 0) return fail(MOE_ERR_INVALID, "splits must divide f / 64");
+  if (splits < 1 || (f / 128) % splits != 0) return fail(MOE_ERR_INVALID, "splits must divide f / 128");
   if (T == 0) return MOE_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const auto* hh = static_cast<const _Float16*>(h);
   const auto* sc = static_cast<const uint16_t*>(scales);
   if (T <= moe::kDecodeMaxT)
-    MOE_HIP(moe::launch_down_decode(hh, offsets, w_down, sc, y, splits, T * k, d, f, E, s), "down");
+    MOE_HIP(moe::launch_down_decode(hh, offsets, w_down, sc, y, splits, T * k, T, d, f, E, s), "down");
   else
     MOE_HIP(moe::launch_down_prefill(hh, offsets, w_down, sc, y, splits, T * k, d, f, E, s), "down");
   return MOE_OK;

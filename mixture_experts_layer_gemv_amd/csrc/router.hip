@@ -1,45 +1,66 @@
 // Router: fp32 logits, softmax and top-k selection (Grok-1 Admin & Architecture Guide,
 // section 3 "Mixture of Experts", steps 1-2; routing and softmax in fp32, section 9).
 //
-// One wavefront per token. Lane l accumulates the logits of all E experts over the
-// input features i = 8 l + 512 s + r (a 16-byte bf16 load of x and the matching rows of
-// router_w per step), then a butterfly reduction over the 64 lanes gives every lane the
-// same fp32 logits (the xor-pairing makes each lane add the same two values, so the
-// result is identical in all lanes and run to run). Every lane then computes the softmax
-// (max-subtracted, denominator summed in expert order) and picks the k largest
-// probabilities, ties to the lower index; lane j < k writes slot j.
+// One workgroup of 256 threads per token. Thread i takes the 8 input features
+// 8 i + 2048 s .. + 7 (s = 0, 1, ...): one 16-byte load of x and the 8 matching rows of
+// router_w (8 E contiguous floats), all issued before use. Partial logits are reduced by
+// a butterfly over each wavefront (the xor pairing makes every lane add the same two
+// values, so all lanes agree bit for bit) and then over the 4 wavefronts in a fixed order
+// through LDS, so the logits are identical run to run. Every lane of wavefront 0 then
+// computes the softmax (max-subtracted, denominator summed in expert order) and picks
+// the k largest probabilities, ties to the lower index; lane j < k writes slot j.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace moe {
 
+namespace {
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+}  // namespace
+
 template <int EMAX>
-__global__ __launch_bounds__(256) void router_topk_kernel(const uint16_t* __restrict__ x,
-                                                          const float* __restrict__ router_w,
-                                                          const float* __restrict__ router_bias,
-                                                          const uint8_t* __restrict__ pad_mask,
-                                                          int32_t* __restrict__ topk_ids,
-                                                          float* __restrict__ topk_w, int T, int d,
-                                                          int E, int k) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;  // whole wavefront exits together
+__global__ __launch_bounds__(kThreads) void router_topk_kernel(const uint16_t* __restrict__ x,
+                                                               const float* __restrict__ router_w,
+                                                               const float* __restrict__ router_bias,
+                                                               const uint8_t* __restrict__ pad_mask,
+                                                               int32_t* __restrict__ topk_ids,
+                                                               float* __restrict__ topk_w, int d, int E,
+                                                               int k) {
+  __shared__ float s_part[kWaves][EMAX];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   float acc[EMAX];
 #pragma unroll
   for (int e = 0; e < EMAX; ++e) acc[e] = 0.0f;
 
   const uint16_t* xt = x + (size_t)t * d;
-  for (int i0 = lane * 8; i0 < d; i0 += 512) {
+  for (int i0 = tid * 8; i0 < d; i0 += kThreads * 8) {
     u32x4 xv = *reinterpret_cast<const u32x4*>(xt + i0);
-    uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+    if (EMAX == 8 && E == 8) {
+      // 8 rows x 8 experts = 256 contiguous bytes
+      const f32x4* rw = reinterpret_cast<const f32x4*>(router_w + (size_t)i0 * 8);
+      f32x4 w[16];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      float xf = __uint_as_float((r & 1) ? (xw[r >> 1] & 0xFFFF0000u) : (xw[r >> 1] << 16));
-      const float* row = router_w + (size_t)(i0 + r) * E;
+      for (int q = 0; q < 16; ++q) w[q] = rw[q];
 #pragma unroll
-      for (int e = 0; e < EMAX; ++e)
-        if (e < E) acc[e] += xf * row[e];
+      for (int r = 0; r < 8; ++r) {
+        const float xf = __uint_as_float((r & 1) ? (xw[r >> 1] & 0xFFFF0000u) : (xw[r >> 1] << 16));
+        const f32x4 lo = w[2 * r], hi = w[2 * r + 1];
+        acc[0] += xf * lo.x, acc[1] += xf * lo.y, acc[2] += xf * lo.z, acc[3] += xf * lo.w;
+        acc[4] += xf * hi.x, acc[5] += xf * hi.y, acc[6] += xf * hi.z, acc[7] += xf * hi.w;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float xf = __uint_as_float((r & 1) ? (xw[r >> 1] & 0xFFFF0000u) : (xw[r >> 1] << 16));
+        const float* row = router_w + (size_t)(i0 + r) * E;
+#pragma unroll
+        for (int e = 0; e < EMAX; ++e)
+          if (e < E) acc[e] += xf * row[e];
+      }
     }
   }
 #pragma unroll
@@ -48,9 +69,19 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const uint16_t* __rest
       float v = acc[e];
 #pragma unroll
       for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-      acc[e] = v;
+      if (lane == 0) s_part[wave][e] = v;
     }
   }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e)
+    if (e < E) {
+      float v = s_part[0][e];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) v += s_part[w][e];
+      acc[e] = v;
+    }
 
   const bool real = pad_mask == nullptr || pad_mask[t] != 0;
   if (!real) {
@@ -101,13 +132,13 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const uint16_t* __rest
 hipError_t launch_router(const uint16_t* x, const float* router_w, const float* router_bias,
                          const uint8_t* pad_mask, int32_t* topk_ids, float* topk_w, int T, int d,
                          int E, int k, hipStream_t stream) {
-  dim3 grid((T + 3) / 4), block(256);
+  dim3 grid(T), block(kThreads);
   if (E <= 8)
-    hipLaunchKernelGGL(router_topk_kernel<8>, grid, block, 0, stream, x, router_w, router_bias,
-                       pad_mask, topk_ids, topk_w, T, d, E, k);
+    hipLaunchKernelGGL(router_topk_kernel<8>, grid, block, 0, stream, x, router_w, router_bias, pad_mask,
+                       topk_ids, topk_w, d, E, k);
   else
     hipLaunchKernelGGL(router_topk_kernel<64>, grid, block, 0, stream, x, router_w, router_bias,
-                       pad_mask, topk_ids, topk_w, T, d, E, k);
+                       pad_mask, topk_ids, topk_w, d, E, k);
   return hipGetLastError();
 }
 

@@ -354,14 +354,21 @@ def test_token_permutation_commutes(T):
     assert err <= 1e-5
 
 
-def test_doubling_down_or_up_scales_doubles_out_exactly():
-    inp, d = small_case("lin", T=64, d=256, f=512)
-    a, _ = run_forward(d, 64, 256, 512, 8, 2)
-    for sl in (slice(1024, None), slice(512, 1024)):
-        sc = d["scales"].clone()
-        sc[:, sl] *= 2
-        b, _ = run_forward(dict(d, scales=sc), 64, 256, 512, 8, 2)
-        assert np.array_equal(b, 2 * a)
+@pytest.mark.parametrize("T", [64, 300])
+def test_doubling_down_scales_doubles_out_exactly(T):
+    # y = s_d * acc and out = sum_j w_j y_j: a power-of-two scale passes through exactly.
+    # (Doubling the up scales doubles h in fp32, but its fp16 rounding is not scale-free
+    # where h is fp16-subnormal, so that one is checked to the output tolerance only.)
+    inp, d = small_case("lin", T=T, d=256, f=512)
+    a, _ = run_forward(d, T, 256, 512, 8, 2)
+    sc = d["scales"].clone()
+    sc[:, 1024:] *= 2
+    b, _ = run_forward(dict(d, scales=sc), T, 256, 512, 8, 2)
+    assert np.array_equal(b, 2 * a)
+    sc = d["scales"].clone()
+    sc[:, 512:1024] *= 2
+    b, _ = run_forward(dict(d, scales=sc), T, 256, 512, 8, 2)
+    assert np.max(np.abs(b - 2 * a)) <= 1e-3 * rms(2 * a)
 
 
 def test_decode_and_prefill_kernels_agree():
