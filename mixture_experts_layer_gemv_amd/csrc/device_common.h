@@ -83,11 +83,12 @@ struct Mfma<f16x8> {
 
 // tanh-form GeLU, 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))), written as
 // v * sigmoid(2 sqrt(2/pi) (v + 0.044715 v^3)) (the same function: 0.5 (1 + tanh z) =
-// 1 / (1 + exp(-2 z))). Saturates cleanly: exp -> inf gives -0, exp -> 0 gives v.
+// 1 / (1 + exp(-2 z))), with the hardware reciprocal (1 ulp). Saturates cleanly:
+// exp -> inf gives -0, exp -> 0 gives v.
 __device__ __forceinline__ float gelu_tanh(float v) {
   const float c2 = 2.0f * 0.7978845608028654f;
   float z = c2 * (v + 0.044715f * v * v * v);
-  return v / (1.0f + __expf(-z));
+  return v * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
 __device__ __forceinline__ u32x4 zero_u32x4() {

@@ -127,7 +127,8 @@ __global__ __launch_bounds__(128) void gate_up_decode_kernel(
   const int row0 = offsets[e];
   const int M = offsets[e + 1] - row0;
   if (M <= 0) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, kg = lane >> 4, cl = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wavefront
+  const int lane = threadIdx.x & 63, kg = lane >> 4, cl = lane & 15;
   const int nl = 8 * cl;  // first of the lane's 8 columns within the slab
   const int n0 = blockIdx.x * kSlab + nl;
   const __amdgpu_buffer_rsrc_t wr = weight_rsrc((wave == 0 ? w_gate : w_up) + (size_t)e * d * f, (size_t)d * f);

@@ -18,9 +18,12 @@
 //     operand is one 16-byte LDS read; column 2 c + q of a 64-column group goes to LDS
 //     row 32 q + c, which gives each lane 2 adjacent output columns in the epilogue.
 // Rows are gathered through the dispatch permutation (gate/up) or read in segment order
-// (down). Tiles are assigned on the device: blockIdx.x enumerates the m-tiles of all
-// expert segments in expert order (read from offsets); surplus slots exit at once.
+// (down). Tiles are assigned on the device: m-slots enumerate the m-tiles of all expert
+// segments in expert order (read from offsets), surplus slots exit at once; the order of
+// (m-slot, n-tile) over workgroups is XCD-aware (tile_of).
 // Scales, GeLU and the fp16 rounding of h are applied in fp32 after the contraction.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -31,7 +34,7 @@ constexpr int BM = 256;         // rows per workgroup tile
 constexpr int BK = 64;          // contraction depth per slice
 constexpr int HALF = 128;       // columns per weight half-tile
 constexpr int LDS_LD = BK + 8;  // 16-bit elements per LDS row (16-byte pad)
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int A_ELEMS = BM * LDS_LD;
 constexpr int B_ELEMS = 2 * HALF * LDS_LD;
 constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;  // 36864 x 2 B = 72 KiB per buffer
@@ -106,79 +109,92 @@ __device__ __forceinline__ void store_col(uint16_t* sB, int row, int koff, const
 //          output H fp16 = gelu_tanh(s_g g) * (s_u u).
 // !kGateUp: A = H rows (fp16), B halves = down columns n0..n0+127 and n0+128..n0+255,
 //          output Y fp32 (part blockIdx.z of the contraction) = s_d y.
+// Workgroup -> tile order. Workgroups go to the 8 XCDs round-robin by linear id, so XCD
+// x runs ids x, x + 8, ... in order. XCD x owns the m-slots x, x + 8, x + 16, ... and walks
+// the n-tiles in groups of `ngroup`, m-slot by m-slot inside a group: the 32 workgroups an
+// XCD holds at once share a few activation tiles and a few weight tiles in its L2, and
+// all XCDs sweep the same weight tiles at the same time.
+__device__ __forceinline__ void tile_of(int w, int nslots, int ngroup, int& mslot, int& ntile) {
+  const int xcd = w & 7, l = w >> 3;
+  const int per_xcd = nslots >> 3;
+  const int g = l / (ngroup * per_xcd), rem = l - g * ngroup * per_xcd;
+  mslot = xcd + 8 * (rem / ngroup);
+  ntile = g * ngroup + rem % ngroup;
+}
+
 template <bool kGateUp>
-__global__ __launch_bounds__(kThreads, 1) void expert_prefill_kernel(
+__global__ __launch_bounds__(kThreads) void expert_prefill_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, const int8_t* __restrict__ B0,
     const int8_t* __restrict__ B1, const uint16_t* __restrict__ scales, void* __restrict__ out,
-    int d, int f, int E, int rows_cap) {
+    int d, int f, int E, int rows_cap, int nslots, int ngroup) {
   using Frag = typename PrefillTraits<kGateUp>::Frag;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE_ELEMS];
 
+  int mslot, ntile;
+  tile_of(blockIdx.x, nslots, ngroup, mslot, ntile);
   int e, row0, rows;
-  if (!find_tile(offsets, E, blockIdx.x, e, row0, rows)) return;
+  if (!find_tile(offsets, E, mslot, e, row0, rows)) return;
 
   const int K = kGateUp ? d : f;  // contraction length
   const int N = kGateUp ? f : d;  // columns of each weight matrix
   const int kspan = K / gridDim.z, kbeg = blockIdx.z * kspan;
-  const int n0 = blockIdx.y * (kGateUp ? HALF : 2 * HALF);
+  const int n0 = ntile * (kGateUp ? HALF : 2 * HALF);
   const uint32_t ldb = (uint32_t)N;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 1, wn = wave & 1;  // 4 x 2 wavefronts, 64 rows x 128 columns each
 
   // ---- global -> register loads of one slice
-  // A: rows tid / 8 + 32 i (i = 0..7), 16-byte chunk tid % 8 of the slice
-  const uint16_t* arow[8];
+  // A: rows tid / 8 + 64 i (i = 0..3), 16-byte chunk tid % 8 of the slice
+  const uint16_t* arow[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int m = min(tid / 8 + 32 * i, rows - 1);  // rows past the tile end repeat a live row
+  for (int i = 0; i < 4; ++i) {
+    const int m = min(tid / 8 + 64 * i, rows - 1);  // rows past the tile end repeat a live row
     const size_t src_row = kGateUp ? (size_t)perm[row0 + m] : (size_t)(row0 + m);
     arow[i] = A + src_row * K + kbeg + 8 * (tid % 8);
   }
-  // B: columns 4 cg .. 4 cg + 3 of each half, rows 8 kg .. 8 kg + 7 of the slice
-  const int cg = tid % 32, kg = tid / 32;
+  // B: half hb = tid / 256, columns 4 cg .. 4 cg + 3 of it, rows 8 kg .. 8 kg + 7 of the slice
+  const int cg = tid % 32, kg = (tid / 32) % 8;
+  const int hb = __builtin_amdgcn_readfirstlane(tid / 256);  // uniform per wavefront
   const size_t ebytes = (size_t)d * f;
   const int8_t* hbase0 = B0 + (size_t)e * ebytes;
   const int8_t* hbase1 = kGateUp ? B1 + (size_t)e * ebytes : hbase0;
-  const __amdgpu_buffer_rsrc_t br0 =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(hbase0), (short)0, (int)ebytes, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t br1 =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(hbase1), (short)0, (int)ebytes, kBufferFlags);
-  const uint32_t bvoff0 = (uint32_t)(8 * kg) * ldb + (uint32_t)(n0 + 4 * cg);
-  const uint32_t bvoff1 = bvoff0 + (kGateUp ? 0u : (uint32_t)HALF);
+  const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(hb == 0 ? hbase0 : hbase1), (short)0, (int)ebytes, kBufferFlags);
+  const uint32_t bvoff = (uint32_t)(8 * kg) * ldb + (uint32_t)(n0 + 4 * cg) + (kGateUp ? 0u : (uint32_t)(HALF * hb));
   // LDS row of the thread's column jj: half h, group cg / 16, column 4 (cg % 16) + jj
   //   -> h * 128 + (cg / 16) * 64 + 32 (jj % 2) + 2 (cg % 16) + jj / 2
   const int brow = (cg / 16) * 64 + 2 * (cg % 16);
 
-  u32x4 ra[8];
+  // two register stages: the loads of slices i + 1 and i + 2 are in flight while slice i
+  // is multiplied out of LDS
+  u32x4 ra[2][4];
   uint32_t rb[2][8];
-  auto gload = [&](int kk) {
+  auto gload = [&](auto stage, int kk) {
+    constexpr int rs = decltype(stage)::value;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ra[i] = *reinterpret_cast<const u32x4*>(arow[i] + kk);
+    for (int i = 0; i < 4; ++i) ra[rs][i] = *reinterpret_cast<const u32x4*>(arow[i] + kk);
     const uint32_t sbase = (uint32_t)(kbeg + kk) * ldb;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      rb[0][r] = __builtin_amdgcn_raw_buffer_load_b32(br0, bvoff0, sbase + r * ldb, 0);
-      rb[1][r] = __builtin_amdgcn_raw_buffer_load_b32(br1, bvoff1, sbase + r * ldb, 0);
-    }
+    for (int r = 0; r < 8; ++r) rb[rs][r] = __builtin_amdgcn_raw_buffer_load_b32(br, bvoff, sbase + r * ldb, 0);
   };
-  auto lds_store = [&](uint16_t* st) {
+  auto lds_store = [&](auto stage, uint16_t* st) {
+    constexpr int rs = decltype(stage)::value;
     uint16_t* sA = st;
     uint16_t* sB = st + A_ELEMS;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<u32x4*>(sA + (size_t)(tid / 8 + 32 * i) * LDS_LD + 8 * (tid % 8)) = ra[i];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      store_col<kGateUp, 0>(sB, h * HALF + brow + 0, 8 * kg, rb[h]);
-      store_col<kGateUp, 1>(sB, h * HALF + brow + 32, 8 * kg, rb[h]);
-      store_col<kGateUp, 2>(sB, h * HALF + brow + 1, 8 * kg, rb[h]);
-      store_col<kGateUp, 3>(sB, h * HALF + brow + 33, 8 * kg, rb[h]);
-    }
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(sA + (size_t)(tid / 8 + 64 * i) * LDS_LD + 8 * (tid % 8)) = ra[rs][i];
+    store_col<kGateUp, 0>(sB, hb * HALF + brow + 0, 8 * kg, rb[rs]);
+    store_col<kGateUp, 1>(sB, hb * HALF + brow + 32, 8 * kg, rb[rs]);
+    store_col<kGateUp, 2>(sB, hb * HALF + brow + 1, 8 * kg, rb[rs]);
+    store_col<kGateUp, 3>(sB, hb * HALF + brow + 33, 8 * kg, rb[rs]);
   };
+  const std::integral_constant<int, 0> R0{};
+  const std::integral_constant<int, 1> R1{};
 
-  // ---- wavefront tile: rows wm * 128 + 32 mt + (lane % 32); B tiles nt: LDS rows
+  // ---- wavefront tile: rows wm * 64 + 32 mt + (lane % 32); B tiles nt: LDS rows
   //   gate/up: (nt / 2) * 128 + wn * 64 + 32 (nt % 2) + (lane % 32)   (nt 0,1 gate; 2,3 up)
   //   down:    wn * 128 + (nt / 2) * 64 + 32 (nt % 2) + (lane % 32)
   int bro[4];
@@ -186,39 +202,60 @@ __global__ __launch_bounds__(kThreads, 1) void expert_prefill_kernel(
   for (int nt = 0; nt < 4; ++nt)
     bro[nt] = (kGateUp ? (nt >> 1) * HALF + wn * 64 : wn * HALF + (nt >> 1) * 64) + 32 * (nt & 1) + (lane & 31);
   const int kq = 8 * (lane >> 5);
-  const int arl = wm * 128 + (lane & 31);
+  const int arl = wm * 64 + (lane & 31);
 
-  f32x16 acc[4][4];
+  f32x16 acc[2][4];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.0f;
 
   const int nslices = kspan / BK;
-  gload(0);
-  lds_store(lds);
-  __syncthreads();
-  for (int it = 0; it < nslices; ++it) {
-    const uint16_t* cur = lds + (it & 1) * STAGE_ELEMS;
-    if (it + 1 < nslices) gload((it + 1) * BK);
-    const uint16_t* sA = cur;
-    const uint16_t* sB = cur + A_ELEMS;
+  Frag af[2][2], bfr[2][4];
+  auto read_frags = [&](const uint16_t* st, int buf, int ks) {
+    const uint16_t* sA = st;
+    const uint16_t* sB = st + A_ELEMS;
 #pragma unroll
-    for (int ks = 0; ks < BK; ks += 16) {
-      Frag af[4];
+    for (int mt = 0; mt < 2; ++mt)
+      af[buf][mt] = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(sA + (size_t)(arl + 32 * mt) * LDS_LD + ks + kq));
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        af[mt] = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(sA + (size_t)(arl + 32 * mt) * LDS_LD + ks + kq));
+    for (int nt = 0; nt < 4; ++nt)
+      bfr[buf][nt] = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(sB + (size_t)bro[nt] * LDS_LD + ks + kq));
+  };
+  auto mfmas = [&](int buf) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const Frag bfr = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(sB + (size_t)bro[nt] * LDS_LD + ks + kq));
+    for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = Mfma32<Frag>::run(af[mt], bfr, acc[mt][nt]);
-      }
+      for (int mt = 0; mt < 2; ++mt) acc[mt][nt] = Mfma32<Frag>::run(af[buf][mt], bfr[buf][nt], acc[mt][nt]);
+  };
+  // One slice: 4 sub-steps of 16 k; the fragments of sub-step kk + 1 are read before the
+  // MFMAs of sub-step kk.
+  auto slice = [&](const uint16_t* cur) {
+    read_frags(cur, 0, 0);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      if (kk + 1 < BK / 16) read_frags(cur, (kk + 1) & 1, (kk + 1) * 16);
+      mfmas(kk & 1);
     }
-    if (it + 1 < nslices) lds_store(lds + ((it + 1) & 1) * STAGE_ELEMS);
+  };
+
+  // slices it (even) and it + 1 (odd) per trip; nslices is a multiple of 4
+  uint16_t* L0 = lds;
+  uint16_t* L1 = lds + STAGE_ELEMS;
+  gload(R0, 0);
+  gload(R1, BK);
+  lds_store(R0, L0);
+  __syncthreads();
+  for (int it = 0; it < nslices; it += 2) {
+    if (it + 2 < nslices) gload(R0, (it + 2) * BK);
+    slice(L0);
+    lds_store(R1, L1);
+    __syncthreads();
+    if (it + 3 < nslices) gload(R1, (it + 3) * BK);
+    slice(L1);
+    if (it + 2 < nslices) lds_store(R0, L0);
     __syncthreads();
   }
 
@@ -235,10 +272,10 @@ __global__ __launch_bounds__(kThreads, 1) void expert_prefill_kernel(
     const float su0 = bf16_bits_to_float(u2 & 0xFFFFu), su1 = bf16_bits_to_float(u2 >> 16);
     _Float16* H = reinterpret_cast<_Float16*>(out);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int m = wm * 128 + 32 * mt + 8 * (i >> 2) + rq + (i & 3);
+        const int m = wm * 64 + 32 * mt + 8 * (i >> 2) + rq + (i & 3);
         if (m < rows) {
           const float h0 = gelu_tanh(acc[mt][0][i] * sg0) * (acc[mt][2][i] * su0);
           const float h1 = gelu_tanh(acc[mt][1][i] * sg1) * (acc[mt][3][i] * su1);
@@ -253,10 +290,10 @@ __global__ __launch_bounds__(kThreads, 1) void expert_prefill_kernel(
       const uint32_t s2 = *reinterpret_cast<const uint32_t*>(sc + 2 * (size_t)f + n);
       const float sd0 = bf16_bits_to_float(s2 & 0xFFFFu), sd1 = bf16_bits_to_float(s2 >> 16);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int m = wm * 128 + 32 * mt + 8 * (i >> 2) + rq + (i & 3);
+          const int m = wm * 64 + 32 * mt + 8 * (i >> 2) + rq + (i & 3);
           if (m < rows) {
             u32x2 v = {__float_as_uint(acc[mt][2 * g][i] * sd0), __float_as_uint(acc[mt][2 * g + 1][i] * sd1)};
             *reinterpret_cast<u32x2*>(Y + (size_t)(row0 + m) * d + n) = v;
@@ -266,24 +303,31 @@ __global__ __launch_bounds__(kThreads, 1) void expert_prefill_kernel(
   }
 }
 
-int prefill_mslots(int rows_cap, int E) { return (rows_cap + BM - 1) / BM + E; }
+// m-slots: enough for every expert segment's m-tiles (sum of ceil(M_e / BM) <= rows / BM
+// + E), rounded up to a multiple of the 8 XCDs.
+int prefill_mslots(int rows_cap, int E) { return ((rows_cap + BM - 1) / BM + E + 7) / 8 * 8; }
+
+int prefill_ngroup(int ntiles) { return ntiles % 4 == 0 ? 4 : (ntiles % 2 == 0 ? 2 : 1); }
 
 hipError_t launch_gate_up_prefill(const uint16_t* x, const int32_t* perm, const int32_t* offsets,
                                   const int8_t* w_gate, const int8_t* w_up, const uint16_t* scales,
                                   _Float16* H, int rows_cap, int d, int f, int E, hipStream_t stream) {
-  dim3 grid(prefill_mslots(rows_cap, E), f / HALF, 1);
+  const int nslots = prefill_mslots(rows_cap, E), ntiles = f / HALF;
+  dim3 grid(nslots * ntiles, 1, 1);
   hipLaunchKernelGGL(expert_prefill_kernel<true>, grid, dim3(kThreads), 0, stream, x, perm, offsets,
-                     w_gate, w_up, scales, (void*)H, d, f, E, rows_cap);
+                     w_gate, w_up, scales, (void*)H, d, f, E, rows_cap, nslots, prefill_ngroup(ntiles));
   return hipGetLastError();
 }
 
 hipError_t launch_down_prefill(const _Float16* H, const int32_t* offsets, const int8_t* w_down,
                                const uint16_t* scales, float* Y, int splits, int rows_cap, int d,
                                int f, int E, hipStream_t stream) {
-  dim3 grid(prefill_mslots(rows_cap, E), d / (2 * HALF), splits);
+  const int nslots = prefill_mslots(rows_cap, E), ntiles = d / (2 * HALF);
+  dim3 grid(nslots * ntiles, 1, splits);
   hipLaunchKernelGGL(expert_prefill_kernel<false>, grid, dim3(kThreads), 0, stream,
                      reinterpret_cast<const uint16_t*>(H), (const int32_t*)nullptr, offsets, w_down,
-                     (const int8_t*)nullptr, scales, (void*)Y, d, f, E, rows_cap);
+                     (const int8_t*)nullptr, scales, (void*)Y, d, f, E, rows_cap, nslots,
+                     prefill_ngroup(ntiles));
   return hipGetLastError();
 }
 
