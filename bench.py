@@ -51,6 +51,32 @@ def algorithmic_work(spec, counts):
                 gu_flops=gu_flops, dn_flops=dn_flops, layer_flops=layer_flops)
 
 
+def copy_calibration(nbytes: int, steps: int, warmup: int) -> int:
+    """A plain copy of known size (torch's device-to-device copy kernel): reads and writes
+    nbytes each. Its FETCH_SIZE / WRITE_SIZE counters calibrate the layer's traffic figures,
+    and its rate is the practical streaming bandwidth of the part."""
+    import torch
+
+    torch.cuda.set_device(0)
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({"calibration": "device copy", "bytes_read": nbytes, "bytes_written": nbytes,
+                      "ms_per_copy": round(ms, 5), "read_plus_write_GBs": round(gbs, 1),
+                      "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -60,6 +86,9 @@ def main() -> int:
                     choices=["tiny", "decode", "batched_decode", "prefill", "skewed"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="instead of the layer, time a plain device-to-device copy of BYTES bytes "
+                         "(the reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -74,6 +103,9 @@ def main() -> int:
 
     import mixture_experts_layer_gemv_amd as moe
     import synth
+
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration, args.steps, args.warmup)
 
     spec = synth.CONFIGS[args.workload]
     T, d, f, E, k = spec.T, spec.d, spec.f, spec.E, spec.k
