@@ -51,6 +51,28 @@ def algorithmic_work(spec, counts):
                 gu_flops=gu_flops, dn_flops=dn_flops, layer_flops=layer_flops)
 
 
+def recorded_traffic(workload: str, source: str):
+    """HBM traffic of the gate/up kernel as measured by rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (scaled by the copy calibration) and recorded in profiles/, or None when no record
+    matches this workload and the current kernel source (the counters are void once the
+    kernel changes)."""
+    import glob
+    import hashlib
+    import re
+
+    try:
+        digest = hashlib.sha256(open(os.path.join(ROOT, source), "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for m in re.finditer(r"<!-- traffic-record (\{.*?\}) -->", open(path).read()):
+            rec = json.loads(m.group(1))
+            if rec.get("workload") == workload and rec.get("source") == source and rec.get("source_sha256_16") == digest:
+                rec["profile"] = os.path.relpath(path, ROOT)
+                return rec
+    return None
+
+
 def copy_calibration(nbytes: int, steps: int, warmup: int) -> int:
     """A plain copy of known size (torch's device-to-device copy kernel): reads and writes
     nbytes each. Its FETCH_SIZE / WRITE_SIZE counters calibrate the layer's traffic figures,
@@ -191,8 +213,11 @@ def main() -> int:
     if decode:
         gu_ach = work["gu_bytes"] / (gu_ms * 1e-3) / 1e9
         dn_ach = work["dn_bytes"] / (dn_ms * 1e-3) / 1e9
+        rec = recorded_traffic(args.workload, "mixture_experts_layer_gemv_amd/csrc/expert_decode.hip")
         roof = {"bound": "hbm", "achieved": round(gu_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gu_ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "gate_up_decode_kernel",
+                "frac": round(gu_ach / HBM_PEAK_GBS, 4),
+                "traffic": rec["gate_up_traffic_bytes"] if rec else None,
+                "traffic_source": rec["profile"] if rec else None, "kernel": "gate_up_decode_kernel",
                 "algorithmic_bytes_per_launch": work["gu_bytes"], "avg_launch_ms": round(gu_ms, 5)}
         kern = {"down_decode_kernel": {"avg_launch_ms": round(dn_ms, 5), "achieved_GBs": round(dn_ach, 1),
                                        "frac": round(dn_ach / HBM_PEAK_GBS, 4),
