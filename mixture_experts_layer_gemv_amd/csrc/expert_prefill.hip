@@ -110,16 +110,25 @@ __device__ __forceinline__ void store_col(uint16_t* sB, int row, int koff, const
 // !kGateUp: A = H rows (fp16), B halves = down columns n0..n0+127 and n0+128..n0+255,
 //          output Y fp32 (part blockIdx.z of the contraction) = s_d y.
 // Workgroup -> tile order. Workgroups go to the 8 XCDs round-robin by linear id, so XCD
-// x runs ids x, x + 8, ... in order. XCD x owns the m-slots x, x + 8, x + 16, ... and walks
-// the n-tiles in groups of `ngroup`, m-slot by m-slot inside a group: the 32 workgroups an
-// XCD holds at once share a few activation tiles and a few weight tiles in its L2, and
-// all XCDs sweep the same weight tiles at the same time.
-__device__ __forceinline__ void tile_of(int w, int nslots, int ngroup, int& mslot, int& ntile) {
+// x runs ids x, x + 8, ... in order. The XCDs form an xm x xn grid: XCD x owns the m-slots
+// congruent to x / xn (mod xm) and the x % xn-th contiguous block of n-tiles, and walks
+// its n-tiles in groups of `ngroup`, m-slot by m-slot inside a group. So each weight tile
+// is streamed from HBM by xm XCDs only (xm = 1 for gate/up), the activation tiles are
+// re-read from the last-level cache, and the 32 workgroups an XCD holds at once share a
+// few activation and weight tiles in its L2.
+struct TileOrder {
+  int nslots, ntiles, xm, xn, ngroup;
+};
+
+__device__ __forceinline__ void tile_of(int w, const TileOrder& o, int& mslot, int& ntile) {
   const int xcd = w & 7, l = w >> 3;
-  const int per_xcd = nslots >> 3;
-  const int g = l / (ngroup * per_xcd), rem = l - g * ngroup * per_xcd;
-  mslot = xcd + 8 * (rem / ngroup);
-  ntile = g * ngroup + rem % ngroup;
+  const int xi = xcd / o.xn, xj = xcd - xi * o.xn;
+  const int ms = o.nslots / o.xm;            // m-slots per XCD
+  const int nblk = o.ntiles / o.xn;          // n-tiles per XCD
+  const int per_group = ms * o.ngroup;
+  const int g = l / per_group, rem = l - g * per_group;
+  mslot = xi + o.xm * (rem / o.ngroup);
+  ntile = xj * nblk + g * o.ngroup + rem % o.ngroup;
 }
 
 template <bool kGateUp>
@@ -127,12 +136,12 @@ __global__ __launch_bounds__(kThreads) void expert_prefill_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, const int8_t* __restrict__ B0,
     const int8_t* __restrict__ B1, const uint16_t* __restrict__ scales, void* __restrict__ out,
-    int d, int f, int E, int rows_cap, int nslots, int ngroup) {
+    int d, int f, int E, int rows_cap, TileOrder order) {
   using Frag = typename PrefillTraits<kGateUp>::Frag;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE_ELEMS];
 
   int mslot, ntile;
-  tile_of(blockIdx.x, nslots, ngroup, mslot, ntile);
+  tile_of(blockIdx.x, order, mslot, ntile);
   int e, row0, rows;
   if (!find_tile(offsets, E, mslot, e, row0, rows)) return;
 
@@ -307,15 +316,34 @@ __global__ __launch_bounds__(kThreads) void expert_prefill_kernel(
 // + E), rounded up to a multiple of the 8 XCDs.
 int prefill_mslots(int rows_cap, int E) { return ((rows_cap + BM - 1) / BM + E + 7) / 8 * 8; }
 
-int prefill_ngroup(int ntiles) { return ntiles % 4 == 0 ? 4 : (ntiles % 2 == 0 ? 2 : 1); }
+// xn = n-tile blocks across XCDs (the rest of the 8 split the m-slots), as preferred by
+// the caller when the tile counts allow it; ngroup = n-tiles swept together.
+TileOrder make_order(int nslots, int ntiles, int xn_pref) {
+  TileOrder o{nslots, ntiles, 8, 1, 1};
+  for (int xn = xn_pref; xn >= 1; xn /= 2)
+    if (ntiles % xn == 0) {
+      o.xn = xn;
+      o.xm = 8 / xn;
+      break;
+    }
+  const int nblk = ntiles / o.xn;
+  for (int g : {8, 4, 3, 2, 1})
+    if (nblk % g == 0) {
+      o.ngroup = g;
+      break;
+    }
+  return o;
+}
 
 hipError_t launch_gate_up_prefill(const uint16_t* x, const int32_t* perm, const int32_t* offsets,
                                   const int8_t* w_gate, const int8_t* w_up, const uint16_t* scales,
                                   _Float16* H, int rows_cap, int d, int f, int E, hipStream_t stream) {
   const int nslots = prefill_mslots(rows_cap, E), ntiles = f / HALF;
+  // the activations fit the last-level cache: every XCD takes its own weight columns
+  const TileOrder order = make_order(nslots, ntiles, 8);
   dim3 grid(nslots * ntiles, 1, 1);
   hipLaunchKernelGGL(expert_prefill_kernel<true>, grid, dim3(kThreads), 0, stream, x, perm, offsets,
-                     w_gate, w_up, scales, (void*)H, d, f, E, rows_cap, nslots, prefill_ngroup(ntiles));
+                     w_gate, w_up, scales, (void*)H, d, f, E, rows_cap, order);
   return hipGetLastError();
 }
 
@@ -323,11 +351,12 @@ hipError_t launch_down_prefill(const _Float16* H, const int32_t* offsets, const 
                                const uint16_t* scales, float* Y, int splits, int rows_cap, int d,
                                int f, int E, hipStream_t stream) {
   const int nslots = prefill_mslots(rows_cap, E), ntiles = d / (2 * HALF);
+  // H can exceed the last-level cache: split the XCDs 2 (rows) x 4 (columns)
+  const TileOrder order = make_order(nslots, ntiles, 4);
   dim3 grid(nslots * ntiles, 1, splits);
   hipLaunchKernelGGL(expert_prefill_kernel<false>, grid, dim3(kThreads), 0, stream,
                      reinterpret_cast<const uint16_t*>(H), (const int32_t*)nullptr, offsets, w_down,
-                     (const int8_t*)nullptr, scales, (void*)Y, d, f, E, rows_cap, nslots,
-                     prefill_ngroup(ntiles));
+                     (const int8_t*)nullptr, scales, (void*)Y, d, f, E, rows_cap, order);
   return hipGetLastError();
 }
 
