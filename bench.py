@@ -108,6 +108,10 @@ def main() -> int:
                     choices=["tiny", "decode", "batched_decode", "prefill", "skewed"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
+    ap.add_argument("--variant", default="gather", choices=["gather", "dense", "graph", "block"],
+                    help="gather: moe_forward (the headline); dense: the one-hot-gated formulation; "
+                         "graph: moe_forward replayed from a captured HIP graph; block: the MoE block with "
+                         "the pre-norm and post-norm + residual fused")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the layer, time a plain device-to-device copy of BYTES bytes "
                          "(the reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -156,6 +160,23 @@ def main() -> int:
     step(dbg={"counts": counts_t})  # allocates the library workspace (synchronising), outside timing
     torch.cuda.synchronize()
     counts = counts_t.cpu().tolist()
+    graph = None
+    if args.variant == "dense":
+        def step(dbg=None):  # noqa: F811
+            moe.moe_forward_dense(x, wr, wg, wu, wd, sc, pad, out, T, d, f, E, k, stream, router_bias=bias)
+    elif args.variant == "graph":
+        graph = moe.Graph(x, wr, wg, wu, wd, sc, pad, out, T, d, f, E, k, router_bias=bias)
+
+        def step(dbg=None):  # noqa: F811
+            graph.launch(stream)
+    elif args.variant == "block":
+        ones = torch.ones(d, dtype=torch.float32, device=dev)
+
+        def step(dbg=None):  # noqa: F811
+            moe.moe_block_forward(x, ones, ones, 1e-5, wr, wg, wu, wd, sc, pad, out, T, d, f, E, k, stream,
+                                  router_bias=bias)
+    step()
+    torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -169,7 +190,15 @@ def main() -> int:
     ev1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
-    log(f"{args.steps} steps: {ms_per_step:.4f} ms/step")
+    log(f"{args.steps} steps: {ms_per_step:.4f} ms/step ({args.variant})")
+    if args.variant != "gather":
+        print(json.dumps({"metric": METRIC, "value": round(T / (ms_per_step * 1e-3), 2), "unit": "tokens/s",
+                          "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                          "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+                          "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "variant": args.variant,
+                          "config": {"workload": f"{args.workload}: {spec.description}", "T": T, "d": d, "f": f,
+                                     "E": E, "k": k, "n_pad": spec.n_pad}}), flush=True)
+        return 0
 
     # ---- per-kernel durations: the same kernels through the stage entry points, with HIP
     #      events recorded on the launch stream around the two expert kernels

@@ -133,6 +133,52 @@ int moe_down_splits(int T, int d, int f, int E, int k);
 int moe_combine(const float* y, int splits, const int32_t* pos, const float* topk_w,
                 const uint8_t* pad_mask, float* out, int T, int d, int k, void* stream);
 
+/* The dense one-hot-gated formulation the sources describe for their own implementation
+   (Guide section 3, MoE step 4 and the warning under it): every one of the E experts runs
+   on every real token and out[t] = sum over e (in order) of gate[t][e] * y_e(t), where
+   gate[t][e] is the routing weight of e if the router selected it and 0 otherwise. Same
+   arguments, layouts, errors and result (up to the order of the fp32 additions) as
+   moe_forward_ex without dbg; E / k times the expert work. A baseline for the gather path,
+   not a faster one. T * E must not exceed 2^24. Workspace: moe_workspace_bytes_dense. */
+int moe_forward_dense(const void* x, const float* router_w, const int8_t* w_gate, const int8_t* w_up,
+                      const int8_t* w_down, const void* scales, const uint8_t* pad_mask, float* out,
+                      int T, int d, int f, int E, int k, void* stream, const float* router_bias,
+                      void* workspace, size_t workspace_bytes);
+size_t moe_workspace_bytes_dense(int T, int d, int f, int E, int k);
+
+/* The MoE block of a decoder layer with its neighbours fused (Guide section 3 "Transformer
+   stack": pre- and post-norm RMSNorm around the MoE block and the residual h += h_dense;
+   grok-field-guide source map, fourth stop):
+     x     = bf16(h * (1 / sqrt(mean(h^2) + eps)) * norm_pre)   (fused into the router kernel)
+     m     = the layer above on x (same routing, experts and combine)
+     h_out = h + m * (1 / sqrt(mean(m^2) + eps)) * norm_post    (fused into the combine kernel)
+   h bf16 [T][d]; norm_pre, norm_post fp32 [d] (16-byte aligned); eps >= 0; h_out fp32 [T][d].
+   Padded tokens: m = 0, so h_out = h. x_norm_out: optional bf16 [T][d] copy of x (NULL = not
+   wanted). The sources give neither eps nor the norm scales' form; these are the readings.
+   Workspace: moe_workspace_bytes_block. Errors as moe_forward_ex. */
+int moe_block_forward(const void* h, const float* norm_pre, const float* norm_post, float eps,
+                      const float* router_w, const int8_t* w_gate, const int8_t* w_up,
+                      const int8_t* w_down, const void* scales, const uint8_t* pad_mask, float* h_out,
+                      int T, int d, int f, int E, int k, void* stream, const float* router_bias,
+                      void* workspace, size_t workspace_bytes, void* x_norm_out);
+size_t moe_workspace_bytes_block(int T, int d, int f, int E, int k);
+
+/* Single-launch forward (for decode loops with fixed buffers): the router, dispatch,
+   expert and combine launches of one moe_forward_ex call are captured once into a HIP
+   graph; each moe_graph_launch replays all of them with one hipGraphLaunch on `stream`.
+   The graph holds the pointers and shapes given here: every replay reads the inputs'
+   current contents at those addresses and writes out. The workspace (caller's, or the
+   library's, allocated here before the capture) must stay alive and must not be used by
+   overlapping calls. moe_graph_create synchronises nothing but may allocate the library
+   workspace; moe_graph_launch allocates nothing. T must be > 0. */
+typedef struct moe_graph moe_graph;
+int moe_graph_create(moe_graph** graph, const void* x, const float* router_w, const int8_t* w_gate,
+                     const int8_t* w_up, const int8_t* w_down, const void* scales,
+                     const uint8_t* pad_mask, float* out, int T, int d, int f, int E, int k,
+                     const float* router_bias, void* workspace, size_t workspace_bytes);
+int moe_graph_launch(moe_graph* graph, void* stream);
+void moe_graph_destroy(moe_graph* graph);
+
 /* Bytes of device workspace moe_forward needs for a shape (0 for T == 0). */
 size_t moe_workspace_bytes(int T, int d, int f, int E, int k);
 

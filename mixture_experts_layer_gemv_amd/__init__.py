@@ -32,6 +32,13 @@ SIGNATURES = {
     "moe_down_splits": ([_i32] * 5, _i32),
     "moe_combine": ([_vp] + [_i32] + [_vp] * 4 + [_i32] * 3 + [_vp], _i32),
     "moe_workspace_bytes": ([_i32] * 5, _sz),
+    "moe_forward_dense": ([_vp] * 8 + [_i32] * 5 + [_vp, _vp, _vp, _sz], _i32),
+    "moe_workspace_bytes_dense": ([_i32] * 5, _sz),
+    "moe_block_forward": ([_vp, _vp, _vp, ctypes.c_float] + [_vp] * 7 + [_i32] * 5 + [_vp, _vp, _vp, _sz, _vp], _i32),
+    "moe_workspace_bytes_block": ([_i32] * 5, _sz),
+    "moe_graph_create": ([ctypes.POINTER(_vp)] + [_vp] * 8 + [_i32] * 5 + [_vp, _vp, _sz], _i32),
+    "moe_graph_launch": ([_vp, _vp], _i32),
+    "moe_graph_destroy": ([_vp], None),
     "moe_release_workspace": ([], None),
     "moe_last_error": ([], ctypes.c_char_p),
     "moe_abi_version": ([], _i32),
@@ -124,6 +131,59 @@ def moe_forward_ex(x, router_w, w_gate, w_up, w_down, scales, pad_mask, out, T, 
                                 _ptr(pad_mask), _ptr(out), T, d, f, E, k, _stream(stream), _ptr(router_bias),
                                 _ptr(workspace), workspace_bytes_,
                                 ctypes.byref(dbg_struct) if dbg_struct is not None else None))
+
+
+def moe_forward_dense(x, router_w, w_gate, w_up, w_down, scales, pad_mask, out, T, d, f, E, k, stream=None,
+                      router_bias=None, workspace=None, workspace_bytes_: int = 0) -> None:
+    """The dense one-hot-gated formulation (every expert on every token): a baseline."""
+    _check(lib().moe_forward_dense(_ptr(x), _ptr(router_w), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(scales),
+                                   _ptr(pad_mask), _ptr(out), T, d, f, E, k, _stream(stream), _ptr(router_bias),
+                                   _ptr(workspace), workspace_bytes_))
+
+
+def workspace_bytes_dense(T: int, d: int, f: int, E: int, k: int) -> int:
+    return lib().moe_workspace_bytes_dense(T, d, f, E, k)
+
+
+def moe_block_forward(h, norm_pre, norm_post, eps, router_w, w_gate, w_up, w_down, scales, pad_mask, h_out,
+                      T, d, f, E, k, stream=None, router_bias=None, workspace=None, workspace_bytes_: int = 0,
+                      x_norm_out=None) -> None:
+    """The decoder layer's MoE block with the pre-norm and post-norm + residual fused."""
+    _check(lib().moe_block_forward(_ptr(h), _ptr(norm_pre), _ptr(norm_post), float(eps), _ptr(router_w),
+                                   _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(scales), _ptr(pad_mask), _ptr(h_out),
+                                   T, d, f, E, k, _stream(stream), _ptr(router_bias), _ptr(workspace),
+                                   workspace_bytes_, _ptr(x_norm_out)))
+
+
+def workspace_bytes_block(T: int, d: int, f: int, E: int, k: int) -> int:
+    return lib().moe_workspace_bytes_block(T, d, f, E, k)
+
+
+class Graph:
+    """A captured single-launch forward (moe_graph_*): fixed buffers, one hipGraphLaunch per call."""
+
+    def __init__(self, x, router_w, w_gate, w_up, w_down, scales, pad_mask, out, T, d, f, E, k,
+                 router_bias=None, workspace=None, workspace_bytes_: int = 0):
+        handle = _vp()
+        _check(lib().moe_graph_create(ctypes.byref(handle), _ptr(x), _ptr(router_w), _ptr(w_gate), _ptr(w_up),
+                                      _ptr(w_down), _ptr(scales), _ptr(pad_mask), _ptr(out), T, d, f, E, k,
+                                      _ptr(router_bias), _ptr(workspace), workspace_bytes_))
+        self._handle = handle
+        self._keep = (x, router_w, w_gate, w_up, w_down, scales, pad_mask, out, router_bias, workspace)
+
+    def launch(self, stream=None) -> None:
+        _check(lib().moe_graph_launch(self._handle, _stream(stream)))
+
+    def close(self) -> None:
+        if self._handle:
+            lib().moe_graph_destroy(self._handle)
+            self._handle = _vp()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def moe_route(x, router_w, router_bias, pad_mask, topk_ids, topk_w, T, d, E, k, stream=None) -> None:

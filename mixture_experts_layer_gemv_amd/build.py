@@ -12,7 +12,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 
-SOURCES = ["router.hip", "dispatch.hip", "expert_decode.hip", "expert_prefill.hip", "combine.hip", "moe_api.hip"]
+SOURCES = ["router.hip", "dispatch.hip", "expert_decode.hip", "expert_prefill.hip", "combine.hip", "dense_onehot.hip",
+           "moe_api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

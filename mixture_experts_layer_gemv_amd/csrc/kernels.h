@@ -14,6 +14,11 @@ hipError_t launch_router(const uint16_t* x, const float* router_w, const float* 
                          const uint8_t* pad_mask, int32_t* topk_ids, float* topk_w, int T, int d,
                          int E, int k, hipStream_t stream);
 
+hipError_t launch_prenorm_router(const uint16_t* h, const float* norm_pre, float eps, uint16_t* x_norm,
+                                 const float* router_w, const float* router_bias, const uint8_t* pad_mask,
+                                 int32_t* topk_ids, float* topk_w, int T, int d, int E, int k,
+                                 hipStream_t stream);
+
 hipError_t launch_dispatch(const int32_t* ids, const uint8_t* pad_mask, int32_t* counts,
                            int32_t* offsets, int32_t* perm, int32_t* pos, int T, int E, int k,
                            hipStream_t stream);
@@ -34,8 +39,16 @@ hipError_t launch_down_prefill(const _Float16* H, const int32_t* offsets, const 
                                const uint16_t* scales, float* Y, int splits, int rows_cap, int d,
                                int f, int E, hipStream_t stream);
 
+hipError_t launch_onehot_expand(const int32_t* ids, const float* w, const uint8_t* pad_mask,
+                                int32_t* ids_all, float* gates, int T, int E, int k, hipStream_t stream);
+
 hipError_t launch_combine(const float* Y, int splits, size_t part_stride, const int32_t* pos,
                           const float* topk_w, const uint8_t* pad_mask, float* out, int T, int d,
                           int k, hipStream_t stream);
+
+hipError_t launch_combine_postnorm(const float* Y, int splits, size_t part_stride, const int32_t* pos,
+                                   const float* topk_w, const uint8_t* pad_mask, const uint16_t* h,
+                                   const float* norm_post, float eps, float* out, int T, int d, int k,
+                                   hipStream_t stream);
 
 }  // namespace moe

@@ -95,6 +95,27 @@ Layout make_layout(int T, int d, int f, int E, int k) {
   return L;
 }
 
+// Workspace of the dense one-hot formulation: the top-k routing, then the all-expert
+// routing (k' = E) with its one-hot gates, and the regular layout for k' = E after it.
+struct DenseLayout {
+  size_t ids, w, inner, total;
+  Layout L;
+};
+
+DenseLayout make_dense_layout(int T, int d, int f, int E, int k) {
+  DenseLayout D{};
+  size_t at = 0;
+  const size_t tk = (size_t)T * k;
+  D.ids = at;
+  at += round_up(tk * 4, 256);
+  D.w = at;
+  at += round_up(tk * 4, 256);
+  D.inner = at;
+  D.L = make_layout(T, d, f, E, E);
+  D.total = at + D.L.total;
+  return D;
+}
+
 struct DeviceWorkspace {
   void* ptr = nullptr;
   size_t bytes = 0;
@@ -241,6 +262,105 @@ int moe_forward_ex(const void* x, const float* router_w, const int8_t* w_gate, c
   return MOE_OK;
 }
 
+size_t moe_workspace_bytes_dense(int T, int d, int f, int E, int k) {
+  if (check_shape(T, d, f, E, k) != MOE_OK || T == 0) return 0;
+  if ((long long)T * E > kMaxAssignments) return 0;
+  return make_dense_layout(T, d, f, E, k).total;
+}
+
+int moe_forward_dense(const void* x, const float* router_w, const int8_t* w_gate, const int8_t* w_up,
+                      const int8_t* w_down, const void* scales, const uint8_t* pad_mask, float* out, int T,
+                      int d, int f, int E, int k, void* stream, const float* router_bias, void* workspace,
+                      size_t workspace_bytes) {
+  MOE_TRY(check_layer_args(x, router_w, w_gate, w_up, w_down, scales, out, T, d, f, E, k));
+  if (router_bias && !aligned(router_bias, 4)) return fail(MOE_ERR_INVALID, "router_bias is not 4-byte aligned");
+  if ((long long)T * E > kMaxAssignments) return fail(MOE_ERR_UNSUPPORTED, "T * E exceeds 2^24 assignments");
+  if (T == 0) return MOE_OK;
+  const DenseLayout D = make_dense_layout(T, d, f, E, k);
+  char* ws = nullptr;
+  if (workspace) {
+    if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID, "workspace is not 256-byte aligned");
+    if (workspace_bytes < D.total)
+      return fail(MOE_ERR_INVALID, "workspace too small: need " + std::to_string(D.total) + " bytes");
+    ws = static_cast<char*>(workspace);
+  } else {
+    MOE_TRY(library_workspace(D.total, &ws));
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto* ids = reinterpret_cast<int32_t*>(ws + D.ids);
+  auto* w = reinterpret_cast<float*>(ws + D.w);
+  char* in = ws + D.inner;
+  const Layout& L = D.L;
+  auto* ids_all = reinterpret_cast<int32_t*>(in + L.ids);
+  auto* gates = reinterpret_cast<float*>(in + L.w);
+  auto* counts = reinterpret_cast<int32_t*>(in + L.counts);
+  auto* offsets = reinterpret_cast<int32_t*>(in + L.offsets);
+  auto* perm = reinterpret_cast<int32_t*>(in + L.perm);
+  auto* pos = reinterpret_cast<int32_t*>(in + L.pos);
+  auto* h = reinterpret_cast<_Float16*>(in + L.h);
+  auto* y = reinterpret_cast<float*>(in + L.y);
+  const auto* xb = static_cast<const uint16_t*>(x);
+  const auto* sc = static_cast<const uint16_t*>(scales);
+  MOE_HIP(moe::launch_router(xb, router_w, router_bias, pad_mask, ids, w, T, d, E, k, s), "router");
+  MOE_HIP(moe::launch_onehot_expand(ids, w, pad_mask, ids_all, gates, T, E, k, s), "onehot_expand");
+  MOE_HIP(moe::launch_dispatch(ids_all, pad_mask, counts, offsets, perm, pos, T, E, E, s), "dispatch");
+  MOE_TRY(run_experts(xb, perm, offsets, w_gate, w_up, w_down, sc, h, y, L.splits, T, d, f, E, E, s));
+  MOE_HIP(moe::launch_combine(y, L.splits, (size_t)T * E * d, pos, gates, pad_mask, out, T, d, E, s), "combine");
+  return MOE_OK;
+}
+
+size_t moe_workspace_bytes_block(int T, int d, int f, int E, int k) {
+  if (check_shape(T, d, f, E, k) != MOE_OK || T == 0) return 0;
+  return round_up((size_t)T * d * 2, 256) + make_layout(T, d, f, E, k).total;
+}
+
+int moe_block_forward(const void* h, const float* norm_pre, const float* norm_post, float eps,
+                      const float* router_w, const int8_t* w_gate, const int8_t* w_up, const int8_t* w_down,
+                      const void* scales, const uint8_t* pad_mask, float* h_out, int T, int d, int f, int E,
+                      int k, void* stream, const float* router_bias, void* workspace, size_t workspace_bytes,
+                      void* x_norm_out) {
+  MOE_TRY(check_layer_args(h, router_w, w_gate, w_up, w_down, scales, h_out, T, d, f, E, k));
+  MOE_TRY(check_ptr(norm_pre, "norm_pre"));
+  MOE_TRY(check_ptr(norm_post, "norm_post"));
+  if (!(eps >= 0.0f)) return fail(MOE_ERR_INVALID, "eps must be >= 0");
+  if (router_bias && !aligned(router_bias, 4)) return fail(MOE_ERR_INVALID, "router_bias is not 4-byte aligned");
+  if (T == 0) return MOE_OK;
+  const size_t xbytes = round_up((size_t)T * d * 2, 256);
+  const Layout L = make_layout(T, d, f, E, k);
+  const size_t need = xbytes + L.total;
+  char* ws = nullptr;
+  if (workspace) {
+    if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID, "workspace is not 256-byte aligned");
+    if (workspace_bytes < need) return fail(MOE_ERR_INVALID, "workspace too small: need " + std::to_string(need) + " bytes");
+    ws = static_cast<char*>(workspace);
+  } else {
+    MOE_TRY(library_workspace(need, &ws));
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto* xn = reinterpret_cast<uint16_t*>(ws);
+  char* in = ws + xbytes;
+  auto* ids = reinterpret_cast<int32_t*>(in + L.ids);
+  auto* w = reinterpret_cast<float*>(in + L.w);
+  auto* counts = reinterpret_cast<int32_t*>(in + L.counts);
+  auto* offsets = reinterpret_cast<int32_t*>(in + L.offsets);
+  auto* perm = reinterpret_cast<int32_t*>(in + L.perm);
+  auto* pos = reinterpret_cast<int32_t*>(in + L.pos);
+  auto* hh = reinterpret_cast<_Float16*>(in + L.h);
+  auto* y = reinterpret_cast<float*>(in + L.y);
+  const auto* hb = static_cast<const uint16_t*>(h);
+  const auto* sc = static_cast<const uint16_t*>(scales);
+  MOE_HIP(moe::launch_prenorm_router(hb, norm_pre, eps, xn, router_w, router_bias, pad_mask, ids, w, T, d, E, k, s),
+          "prenorm_router");
+  MOE_HIP(moe::launch_dispatch(ids, pad_mask, counts, offsets, perm, pos, T, E, k, s), "dispatch");
+  MOE_TRY(run_experts(xn, perm, offsets, w_gate, w_up, w_down, sc, hh, y, L.splits, T, d, f, E, k, s));
+  MOE_HIP(moe::launch_combine_postnorm(y, L.splits, (size_t)T * k * d, pos, w, pad_mask, hb, norm_post, eps, h_out,
+                                       T, d, k, s),
+          "combine_postnorm");
+  if (x_norm_out)
+    MOE_HIP(hipMemcpyAsync(x_norm_out, xn, (size_t)T * d * 2, hipMemcpyDeviceToDevice, s), "x_norm copy");
+  return MOE_OK;
+}
+
 int moe_forward(const void* x, const float* router_w, const int8_t* w_gate, const int8_t* w_up,
                 const int8_t* w_down, const void* scales, const uint8_t* pad_mask, float* out, int T,
                 int d, int f, int E, int k, void* stream) {
@@ -332,6 +452,71 @@ int moe_combine(const float* y, int splits, const int32_t* pos, const float* top
                               static_cast<hipStream_t>(stream)),
           "combine");
   return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------------------
+// Single-launch forward: the five launches captured once into a HIP graph and replayed.
+
+struct moe_graph {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+int moe_graph_create(moe_graph** out_graph, const void* x, const float* router_w, const int8_t* w_gate,
+                     const int8_t* w_up, const int8_t* w_down, const void* scales, const uint8_t* pad_mask,
+                     float* out, int T, int d, int f, int E, int k, const float* router_bias, void* workspace,
+                     size_t workspace_bytes) {
+  if (!out_graph) return fail(MOE_ERR_INVALID, "out_graph is NULL");
+  *out_graph = nullptr;
+  MOE_TRY(check_layer_args(x, router_w, w_gate, w_up, w_down, scales, out, T, d, f, E, k));
+  if (T == 0) return fail(MOE_ERR_INVALID, "T must be > 0 for a graph");
+  // the workspace must exist before capture: nothing may allocate inside it
+  char* ws = static_cast<char*>(workspace);
+  const size_t need = make_layout(T, d, f, E, k).total;
+  if (!ws) {
+    MOE_TRY(library_workspace(need, &ws));
+  } else if (workspace_bytes < need) {
+    return fail(MOE_ERR_INVALID, "workspace too small: need " + std::to_string(need) + " bytes");
+  }
+  hipStream_t cs = nullptr;
+  MOE_HIP(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking), "hipStreamCreate");
+  auto* g = new moe_graph();
+  int rc = MOE_OK;
+  hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    rc = hip_fail(e, "hipStreamBeginCapture");
+  } else {
+    rc = moe_forward_ex(x, router_w, w_gate, w_up, w_down, scales, pad_mask, out, T, d, f, E, k, cs, router_bias,
+                        ws, need, nullptr);
+    hipError_t e2 = hipStreamEndCapture(cs, &g->graph);
+    if (rc == MOE_OK && e2 != hipSuccess) rc = hip_fail(e2, "hipStreamEndCapture");
+  }
+  if (rc == MOE_OK) {
+    e = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0);
+    if (e != hipSuccess) rc = hip_fail(e, "hipGraphInstantiate");
+  }
+  (void)hipStreamDestroy(cs);
+  if (rc != MOE_OK) {
+    if (g->exec) (void)hipGraphExecDestroy(g->exec);
+    if (g->graph) (void)hipGraphDestroy(g->graph);
+    delete g;
+    return rc;
+  }
+  *out_graph = g;
+  return MOE_OK;
+}
+
+int moe_graph_launch(moe_graph* g, void* stream) {
+  if (!g || !g->exec) return fail(MOE_ERR_INVALID, "graph is NULL");
+  MOE_HIP(hipGraphLaunch(g->exec, static_cast<hipStream_t>(stream)), "hipGraphLaunch");
+  return MOE_OK;
+}
+
+void moe_graph_destroy(moe_graph* g) {
+  if (!g) return;
+  if (g->exec) (void)hipGraphExecDestroy(g->exec);
+  if (g->graph) (void)hipGraphDestroy(g->graph);
+  delete g;
 }
 
 }  // extern "C"

@@ -19,15 +19,40 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 }  // namespace
 
-template <int EMAX>
+// Sum over the workgroup of one value per thread, in a fixed order (butterfly in each
+// wavefront, then the wavefronts in index order); every thread gets the result.
+__device__ __forceinline__ float block_sum(float v, float* s_red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  if (lane == 0) s_red[wave] = v;
+  __syncthreads();
+  float r = s_red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) r += s_red[w];
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float v) {
+  uint32_t u = __float_as_uint(v);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// kNorm: x is the layer input h; the router (and the experts, through x_norm) see
+// x = bf16(h * (1 / sqrt(mean(h^2) + eps)) * norm_pre), the pre-norm of the decoder layer's
+// MoE block (Guide section 3 "Transformer stack": RMSNorm before the MoE block).
+template <int EMAX, bool kNorm>
 __global__ __launch_bounds__(kThreads) void router_topk_kernel(const uint16_t* __restrict__ x,
                                                                const float* __restrict__ router_w,
                                                                const float* __restrict__ router_bias,
                                                                const uint8_t* __restrict__ pad_mask,
                                                                int32_t* __restrict__ topk_ids,
                                                                float* __restrict__ topk_w, int d, int E,
-                                                               int k) {
+                                                               int k, const float* __restrict__ norm_pre,
+                                                               float eps, uint16_t* __restrict__ x_norm) {
   __shared__ float s_part[kWaves][EMAX];
+  __shared__ float s_red[kWaves];
   const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -36,9 +61,35 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(const uint16_t* _
   for (int e = 0; e < EMAX; ++e) acc[e] = 0.0f;
 
   const uint16_t* xt = x + (size_t)t * d;
+  float rnorm = 1.0f;
+  if constexpr (kNorm) {
+    float ss = 0.0f;
+    for (int i0 = tid * 8; i0 < d; i0 += kThreads * 8) {
+      u32x4 xv = *reinterpret_cast<const u32x4*>(xt + i0);
+      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float v = __uint_as_float((r & 1) ? (xw[r >> 1] & 0xFFFF0000u) : (xw[r >> 1] << 16));
+        ss += v * v;
+      }
+    }
+    rnorm = 1.0f / sqrtf(block_sum(ss, s_red) / (float)d + eps);
+  }
   for (int i0 = tid * 8; i0 < d; i0 += kThreads * 8) {
     u32x4 xv = *reinterpret_cast<const u32x4*>(xt + i0);
-    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+    uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+    if constexpr (kNorm) {
+      const f32x4* np4 = reinterpret_cast<const f32x4*>(norm_pre + i0);
+      const f32x4 n0 = np4[0], n1 = np4[1];
+      const float ns[8] = {n0.x, n0.y, n0.z, n0.w, n1.x, n1.y, n1.z, n1.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float v0 = __uint_as_float(xw[q] << 16), v1 = __uint_as_float(xw[q] & 0xFFFF0000u);
+        xw[q] = bf16_rne_bits(v0 * rnorm * ns[2 * q]) | (bf16_rne_bits(v1 * rnorm * ns[2 * q + 1]) << 16);
+      }
+      u32x4 o = {xw[0], xw[1], xw[2], xw[3]};
+      *reinterpret_cast<u32x4*>(x_norm + (size_t)t * d + i0) = o;
+    }
     if (EMAX == 8 && E == 8) {
       // 8 rows x 8 experts = 256 contiguous bytes
       const f32x4* rw = reinterpret_cast<const f32x4*>(router_w + (size_t)i0 * 8);
@@ -134,11 +185,25 @@ hipError_t launch_router(const uint16_t* x, const float* router_w, const float* 
                          int E, int k, hipStream_t stream) {
   dim3 grid(T), block(kThreads);
   if (E <= 8)
-    hipLaunchKernelGGL(router_topk_kernel<8>, grid, block, 0, stream, x, router_w, router_bias, pad_mask,
-                       topk_ids, topk_w, d, E, k);
+    hipLaunchKernelGGL((router_topk_kernel<8, false>), grid, block, 0, stream, x, router_w, router_bias, pad_mask,
+                       topk_ids, topk_w, d, E, k, (const float*)nullptr, 0.0f, (uint16_t*)nullptr);
   else
-    hipLaunchKernelGGL(router_topk_kernel<64>, grid, block, 0, stream, x, router_w, router_bias,
-                       pad_mask, topk_ids, topk_w, d, E, k);
+    hipLaunchKernelGGL((router_topk_kernel<64, false>), grid, block, 0, stream, x, router_w, router_bias,
+                       pad_mask, topk_ids, topk_w, d, E, k, (const float*)nullptr, 0.0f, (uint16_t*)nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_prenorm_router(const uint16_t* h, const float* norm_pre, float eps, uint16_t* x_norm,
+                                 const float* router_w, const float* router_bias, const uint8_t* pad_mask,
+                                 int32_t* topk_ids, float* topk_w, int T, int d, int E, int k,
+                                 hipStream_t stream) {
+  dim3 grid(T), block(kThreads);
+  if (E <= 8)
+    hipLaunchKernelGGL((router_topk_kernel<8, true>), grid, block, 0, stream, h, router_w, router_bias, pad_mask,
+                       topk_ids, topk_w, d, E, k, norm_pre, eps, x_norm);
+  else
+    hipLaunchKernelGGL((router_topk_kernel<64, true>), grid, block, 0, stream, h, router_w, router_bias,
+                       pad_mask, topk_ids, topk_w, d, E, k, norm_pre, eps, x_norm);
   return hipGetLastError();
 }
 

@@ -50,6 +50,11 @@ def _load():
     lib.oracle_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, i32]
     lib.oracle_forward_dense.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32]
     lib.oracle_forward_f64.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
+    lib.oracle_rms_norm_row.argtypes = [vp, vp, ctypes.c_float, i32, vp]
+    lib.oracle_rms_norm_row.restype = None
+    lib.oracle_block_forward.argtypes = [vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                         i32, i32, vp, vp, i32]
+    lib.oracle_block_forward.restype = ctypes.c_int
     for name in ("oracle_route", "oracle_dispatch", "oracle_expert_hidden", "oracle_expert_down",
                  "oracle_forward", "oracle_forward_dense", "oracle_forward_f64"):
         getattr(lib, name).restype = ctypes.c_int
@@ -179,6 +184,31 @@ def forward_f64(x, router_w, router_bias, w_gate, w_up, w_down, scales, pad_mask
                                     _p(out), _p(ids))
     _check(rc, "forward_f64")
     return out, ids
+
+
+def rms_norm_row(v, scale, eps: float):
+    """RMSNorm of one fp32 row (Guide section 3 "Transformer stack"; reading: learned scale, given eps)."""
+    v = np.ascontiguousarray(v, np.float32)
+    out = np.empty_like(v)
+    _load().oracle_rms_norm_row(_p(v), _p(np.ascontiguousarray(scale, np.float32)), eps, v.size, _p(out))
+    return out
+
+
+def block_forward(h, norm_pre, norm_post, eps, router_w, router_bias, w_gate, w_up, w_down, scales, pad_mask,
+                  k: int = 2, nthreads: int = 0):
+    """The decoder layer's MoE block: h + rms_norm(moe(bf16(rms_norm(h)))) (Guide section 3
+    "Transformer stack"; grok-field-guide fourth stop). Returns (h_out fp32 [T][d], x bf16 bits)."""
+    T, d = h.shape
+    E, _, f = w_gate.shape
+    out = np.empty((T, d), np.float32)
+    x = np.empty((T, d), np.uint16)
+    rc = _load().oracle_block_forward(_p(h, np.uint16), _p(np.ascontiguousarray(norm_pre, np.float32)),
+                                      _p(np.ascontiguousarray(norm_post, np.float32)), eps,
+                                      _p(router_w, np.float32), _p(router_bias, np.float32), _p(w_gate, np.int8),
+                                      _p(w_up, np.int8), _p(w_down, np.int8), _p(scales, np.uint16),
+                                      _p(pad_mask, np.uint8), T, d, f, E, k, _p(out), _p(x), nthreads)
+    _check(rc, "block_forward")
+    return out, x
 
 
 def forward_inputs(inp: dict, k: int = 2, nthreads: int = 0, rows=None):

@@ -14,7 +14,10 @@
  *   [G3-cfg]   same guide, section 3 "Configuration objects" (emb_size, num_experts,
  *              num_selected_experts, fprop dtype) and the ffn_size note under the MoE steps
  *   [FG4]      grok-field-guide source-code map, fourth stop (DecoderLayer): the MoE block is
- *              called as moe(rms_norm(h), padding_mask) and its result added to h outside it
+ *              called as moe(rms_norm(h), padding_mask) and its result added to h outside it;
+ *              the page notes that its code leaves out an extra RMSNorm of the source
+ *   [G3-stack] same guide, section 3 "Transformer stack and language model head": pre- and
+ *              post-norm RMSNorm around the FFN/MoE block, residual h += h_dense
  *
  * Arithmetic: fp32 throughout (routing, softmax, expert FFN, combine), every operation
  * rounded on its own (built with -ffp-contract=off), sums taken in index order.
@@ -440,6 +443,52 @@ int oracle_forward_f64(const uint16_t* x, const float* router_w, const float* ro
       }
     }
   }
+  return 0;
+}
+
+/* RMSNorm of one row, fp32: v * (1 / sqrt(mean(v^2) + eps)) * scale, the mean summed in
+   index order. [G3-stack; FG4] (The sources give neither eps nor the scale's form: the
+   reading taken is a learned per-feature fp32 scale and a caller-given eps.) */
+void oracle_rms_norm_row(const float* v, const float* scale, float eps, int d, float* out) {
+  float ss = 0.0f;
+  for (int i = 0; i < d; ++i) ss += v[i] * v[i];
+  const float r = 1.0f / std::sqrt(ss / (float)d + eps);
+  for (int i = 0; i < d; ++i) out[i] = v[i] * r * scale[i];
+}
+
+/* The MoE block of a decoder layer [G3-stack; FG4]:
+     x     = bf16(rms_norm(h; norm_pre))          (the MoE input, rounded to the bf16 fprop dtype)
+     m     = moe(x, pad_mask)                    (oracle_forward)
+     h_out = h + rms_norm(m; norm_post)          (fp32)
+   h bf16 [T][d]; norm_pre, norm_post fp32 [d]; h_out fp32 [T][d]; x_out bf16 [T][d] or NULL.
+   Padded tokens: m = 0, so h_out = h. */
+int oracle_block_forward(const uint16_t* h, const float* norm_pre, const float* norm_post, float eps,
+                         const float* router_w, const float* router_bias, const int8_t* w_gate,
+                         const int8_t* w_up, const int8_t* w_down, const uint16_t* scales,
+                         const uint8_t* pad_mask, int T, int d, int f, int E, int k, float* h_out,
+                         uint16_t* x_out, int nthreads) {
+  if (T < 0 || d <= 0 || f <= 0 || E <= 0 || k <= 0 || k > E) return -1;
+  std::vector<uint16_t> x((size_t)T * d);
+  std::vector<float> row(d), nrm(d);
+  for (int t = 0; t < T; ++t) {
+    for (int i = 0; i < d; ++i) row[i] = bf16_value(h[(size_t)t * d + i]);
+    oracle_rms_norm_row(row.data(), norm_pre, eps, d, nrm.data());
+    for (int i = 0; i < d; ++i) {
+      uint32_t u;
+      std::memcpy(&u, &nrm[i], 4);
+      u += 0x7FFFu + ((u >> 16) & 1u);  // round to nearest even (finite values)
+      x[(size_t)t * d + i] = (uint16_t)(u >> 16);
+    }
+  }
+  std::vector<float> m((size_t)T * d);
+  if (oracle_forward(x.data(), router_w, router_bias, w_gate, w_up, w_down, scales, pad_mask, T, d, f, E, k,
+                     m.data(), nullptr, nullptr, nthreads) != 0)
+    return -1;
+  for (int t = 0; t < T; ++t) {
+    oracle_rms_norm_row(&m[(size_t)t * d], norm_post, eps, d, nrm.data());
+    for (int i = 0; i < d; ++i) h_out[(size_t)t * d + i] = bf16_value(h[(size_t)t * d + i]) + nrm[i];
+  }
+  if (x_out) std::memcpy(x_out, x.data(), sizeof(uint16_t) * x.size());
   return 0;
 }
 

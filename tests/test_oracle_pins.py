@@ -317,3 +317,43 @@ def test_empty_batch():
     inp = small("empty", T=0, d=16, f=16)
     out, ids, w = oracle.forward_inputs(inp)
     assert out.shape == (0, 16) and ids.shape == (0, 2)
+
+
+# ---------------------------------------------------------------- the MoE block of a decoder layer
+
+def test_rms_norm_vs_numpy_and_closed_form():
+    rng = np.random.default_rng(7)
+    v = rng.standard_normal(300).astype(np.float32) * 3
+    scale = (1 + 0.2 * rng.standard_normal(300)).astype(np.float32)
+    got = oracle.rms_norm_row(v, scale, 1e-5)
+    v64 = v.astype(np.float64)
+    ref = v64 / np.sqrt(np.mean(v64 ** 2) + 1e-5) * scale
+    assert np.max(np.abs(got - ref)) <= 1e-6 * np.max(np.abs(ref))
+    # constant row c: rms = |c|, so out = sign(c) * scale / sqrt(1 + eps / c^2)
+    c = np.full(64, -2.5, np.float32)
+    out = oracle.rms_norm_row(c, np.ones(64, np.float32), 0.25)
+    assert np.allclose(out, -1 / np.sqrt(1 + 0.25 / 6.25), rtol=1e-6)
+    # eps matters (catches a dropped eps) and the scale multiplies per feature (catches a dropped scale)
+    assert not np.allclose(oracle.rms_norm_row(c, np.ones(64, np.float32), 0.0), out)
+
+
+def test_block_is_norm_moe_norm_residual():
+    inp = small("block", T=20, d=48, f=64, E=4, n_pad=4)
+    rng = np.random.default_rng(3)
+    wpre = (1 + 0.2 * rng.standard_normal(48)).astype(np.float32)
+    wpost = (1 + 0.2 * rng.standard_normal(48)).astype(np.float32)
+    h_out, x = oracle.block_forward(inp["x"], wpre, wpost, 1e-5, inp["router_w"], None, inp["w_gate"], inp["w_up"],
+                                    inp["w_down"], inp["scales"], inp["pad_mask"])
+    h = bf(inp["x"])
+    # the MoE input is bf16(rms_norm(h)): numpy fp64 value, rounded, within one bf16 ulp
+    xn = h / np.sqrt(np.mean(h ** 2, axis=1, keepdims=True) + 1e-5) * wpre
+    assert np.all(np.abs(bf(x) - xn) <= 2.0 ** -7 * np.abs(xn) + 1e-30)
+    # h_out - h = rms_norm(moe(x)) with the post scale
+    m, _, _ = oracle.forward(x, inp["router_w"], None, inp["w_gate"], inp["w_up"], inp["w_down"], inp["scales"],
+                             inp["pad_mask"])
+    m64 = m.astype(np.float64)
+    post = m64 / np.sqrt(np.mean(m64 ** 2, axis=1, keepdims=True) + 1e-5) * wpost
+    assert np.max(np.abs((h_out - h) - post)) <= 1e-5 * rms(post)
+    # padded tokens: the MoE contributes 0, so h_out = h exactly
+    pad = inp["pad_mask"] == 0
+    assert np.array_equal(h_out[pad], h[pad].astype(np.float32))
