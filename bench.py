@@ -44,11 +44,14 @@ def algorithmic_work(spec, counts):
     gu_bytes = touched * (2 * d * f + 4 * f) + 2 * real * d
     dn_bytes = touched * (d * f + 2 * d)
     layer_bytes = touched * (3 * d * f + 2 * (2 * f + d)) + 2 * spec.T * d + 4 * d * spec.E + 4 * spec.T * d + spec.T
+    # prefill gate/up also writes H once (2 B per element); the decode figure leaves out
+    # that write, which is below 0.1% of its bytes
+    gu_bytes_prefill = touched * (2 * d * f + 4 * f) + 2 * real * d + 2 * n_assign * f
     gu_flops = 4.0 * d * f * n_assign
     dn_flops = 2.0 * d * f * n_assign
     layer_flops = gu_flops + dn_flops + 2.0 * spec.T * d * spec.E
     return dict(touched=touched, n_assign=n_assign, gu_bytes=gu_bytes, dn_bytes=dn_bytes, layer_bytes=layer_bytes,
-                gu_flops=gu_flops, dn_flops=dn_flops, layer_flops=layer_flops)
+                gu_bytes_prefill=gu_bytes_prefill, gu_flops=gu_flops, dn_flops=dn_flops, layer_flops=layer_flops)
 
 
 def recorded_traffic(workload: str, source: str):
@@ -257,10 +260,13 @@ def main() -> int:
     else:
         gu_ach = work["gu_flops"] / (gu_ms * 1e-3) / 1e12
         dn_ach = work["dn_flops"] / (dn_ms * 1e-3) / 1e12
+        rec = recorded_traffic(args.workload, "mixture_experts_layer_gemv_amd/csrc/expert_prefill.hip")
         roof = {"bound": "mfma", "achieved": round(gu_ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(gu_ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(gu_ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": rec["gate_up_traffic_bytes"] if rec else None,
+                "traffic_source": rec["profile"] if rec else None,
                 "kernel": "expert_prefill_kernel<true>", "algorithmic_flops_per_launch": work["gu_flops"],
-                "avg_launch_ms": round(gu_ms, 5)}
+                "algorithmic_bytes_per_launch": work["gu_bytes_prefill"], "avg_launch_ms": round(gu_ms, 5)}
         layer_tf = work["layer_flops"] / (ms_per_step * 1e-3) / 1e12
         kern = {"expert_prefill_kernel<false>": {"avg_launch_ms": round(dn_ms, 5), "achieved_TFLOPs": round(dn_ach, 1),
                                                  "frac": round(dn_ach / MFMA_BF16_PEAK_TFLOPS, 4)},

@@ -3,12 +3,12 @@
 // gelu(linear(x)) * linear_v(x) -> linear_1; "Quantized weights": int8 weights
 // dequantised as q * s with one scale per output channel, compute in bf16.)
 //
-// One workgroup (256 threads, 4 wavefronts in a 2 x 2 arrangement) computes a
-// 256-row x 256-column tile of one expert: for the gate/up kernel 128 columns of gate
+// One workgroup (512 threads, 8 wavefronts in a 4 x 2 arrangement, two per SIMD) computes
+// a 256-row x 256-column tile of one expert: for the gate/up kernel 128 columns of gate
 // and the same 128 of up (so the GeGLU is applied in registers), for the down kernel
-// 256 columns of the down projection. Each wavefront owns 128 rows x 128 columns as
-// 4 x 4 tiles of the 32x32x16 MFMA (256 fp32 accumulators per lane), which keeps the LDS
-// bytes read per MFMA low. The contraction runs in 64-deep slices:
+// 256 columns of the down projection. Each wavefront owns 64 rows x 128 columns as
+// 2 x 4 tiles of the 32x32x16 MFMA (128 fp32 accumulators per lane); the second
+// wavefront on each SIMD covers the other's waits. The contraction runs in 64-deep slices:
 //   * the next slice's activations (16 B per load) and int8 weights (one dword of 4
 //     columns from each of 8 rows per thread and half-tile, through buffer loads whose
 //     row offset is a scalar) are loaded into registers while the current slice's MFMAs
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void expert_prefill_kernel(
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds, per tile (mt, nt), rows wm*128 + 32 mt + 8 (i/4) + 4 (lane/32)
+  // ---- epilogue: lane holds, per tile (mt, nt), rows wm*64 + 32 mt + 8 (i/4) + 4 (lane/32)
   //      + i % 4 (i = 0..15) of column 2 (lane % 32) + (nt % 2) of its 64-column group
   const uint16_t* sc = scales + (size_t)e * (2 * (size_t)f + d);
   const int c2 = 2 * (lane & 31);
