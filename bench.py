@@ -108,7 +108,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode",
-                    choices=["tiny", "decode", "batched_decode", "prefill", "skewed"])
+                    choices=["tiny", "decode", "batched_decode", "prefill", "skewed", "decode_tp8", "prefill_tp8"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     ap.add_argument("--variant", default="gather", choices=["gather", "dense", "graph", "block"],
@@ -289,7 +289,7 @@ def main() -> int:
             oracle.forward_inputs(inp, k=k, nthreads=cores, rows=rows)
             reps += 1
             tok += len(rows)
-            if time.time() - t_start >= args.cpu_seconds or reps >= 50:
+            if time.time() - t_start >= args.cpu_seconds or reps >= 1000:
                 break
         el = time.time() - t_start
         cpu = {"value": round(tok / el, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",

@@ -166,6 +166,7 @@ class Spec:
     w_set: int = 1
     scale_jitter: bool = False
     seed: int = DEFAULT_SEED
+    f_full: Optional[int] = None  # FFN width of the whole layer when f is one GPU's share of it
     description: str = field(default="", compare=False)
 
     @property
@@ -187,6 +188,12 @@ CONFIGS = {
     "skewed": Spec("skewed", T=4096, d=6144, f=32768, n_pad=1024, x_dist="student4", bias=SKEW_BIAS,
                    x_set=5, w_set=2,
                    description="Grok-1 shape, skewed routing: T=4096, 1024 padded, Student-t x, biased router"),
+    # One GPU's share of an 8-way tensor-parallel split over f (all 8 experts, f / 8 columns
+    # of gate/up and rows of down): what each GPU computes before the all-reduce of out.
+    "decode_tp8": Spec("decode_tp8", T=8, d=6144, f=4096, f_full=32768, x_set=2, w_set=6,
+                       description="one GPU's share of 8-way tensor parallelism over f: T=8, d=6144, f=4096"),
+    "prefill_tp8": Spec("prefill_tp8", T=8192, d=6144, f=4096, f_full=32768, x_set=4, w_set=6,
+                        description="one GPU's share of 8-way tensor parallelism over f: T=8192, d=6144, f=4096"),
 }
 
 
@@ -230,8 +237,9 @@ def scales(spec: Spec) -> np.ndarray:
     Value 1/(127 sqrt(fan_in)) in fp64, times a per-channel factor U[0.5, 1.5) when
     scale_jitter is set, rounded fp64 -> fp32 -> bf16 (nearest even both times)."""
     n_ch = 2 * spec.f + spec.d
+    fan_in_down = spec.f_full or spec.f
     base = np.concatenate([np.full(2 * spec.f, 1.0 / (127.0 * math.sqrt(spec.d))),
-                           np.full(spec.d, 1.0 / (127.0 * math.sqrt(spec.f)))])
+                           np.full(spec.d, 1.0 / (127.0 * math.sqrt(fan_in_down)))])
     vals = np.broadcast_to(base, (spec.E, n_ch)).copy()
     if spec.scale_jitter:
         ks = key(spec.seed, 100 + spec.w_set, TENSOR_SCALE)

@@ -45,7 +45,7 @@ def workload(name: str):
     key = ("wl", name)
     if key not in _cache:
         spec = synth.CONFIGS[name]
-        if spec.d == 6144:
+        if spec.d == 6144 and spec.f == 32768 and spec.w_set == 2:
             host_w, dev_w = grok_weights()
             inp = synth.make_inputs(spec, with_weights=False)
             inp.update({n: host_w[n] for n in ("w_gate", "w_up", "w_down")})

@@ -357,3 +357,23 @@ def test_block_is_norm_moe_norm_residual():
     # padded tokens: the MoE contributes 0, so h_out = h exactly
     pad = inp["pad_mask"] == 0
     assert np.array_equal(h_out[pad], h[pad].astype(np.float32))
+
+
+@pytest.mark.parametrize("G", [2, 4])
+def test_tensor_parallel_shares_sum_to_the_layer(G):
+    # Splitting f across G shares (all experts in each) and summing the shares' outputs gives
+    # the layer: routing is per token and replicated, and every term of the down contraction
+    # belongs to exactly one share (Guide section 6, the psum over the model axis).
+    from tp_helpers import tp_share
+
+    inp = small("tp", T=24, d=40, f=96, E=4, k=2, n_pad=3, scale_jitter=True)
+    full, ids, _ = oracle.forward_inputs(inp, k=2)
+    parts = np.zeros(full.shape, np.float64)
+    for g in range(G):
+        sh = tp_share(inp, g, G)
+        out_g, ids_g, _ = oracle.forward_inputs(sh, k=2)
+        assert np.array_equal(ids_g, ids)
+        parts += out_g
+    assert np.max(np.abs(parts - full)) <= 1e-5 * rms(full)
+    # a share on its own is not the layer
+    assert np.max(np.abs(oracle.forward_inputs(tp_share(inp, 0, G), k=2)[0] - full)) > 0.1 * rms(full)
