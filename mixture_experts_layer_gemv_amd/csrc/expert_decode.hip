@@ -5,9 +5,11 @@
 // weights dequantised as q * s, one scale per output channel.)
 //
 // Work split: one wavefront owns a 256-column slab of one matrix of one touched expert
-// and runs down the whole contraction (or one of `splits` parts of it for the down
-// projection). For gate/up a workgroup holds two wavefronts, one per matrix, on the same
-// slab; they meet in LDS for the GeGLU epilogue. Lane l takes the 16 adjacent columns
+// and runs down the whole contraction, or one of `splits` parts of it when the slabs
+// alone are too few to fill the chip (narrow f, e.g. one GPU's share of a tensor-parallel
+// split). For gate/up a workgroup holds two wavefronts, one per matrix, on the same slab;
+// they meet in LDS for the GeGLU epilogue, or, when the contraction is split, write fp32
+// partial sums that geglu_finish_kernel adds in part order before the same epilogue. Lane l takes the 16 adjacent columns
 // n0 + 16 (l % 16) .. + 15 and, per 32-deep step, the rows k0 + 8 (l / 16) .. + 7: eight
 // 16-byte loads, so each row segment a wavefront instruction touches is 256 contiguous
 // bytes. Byte j of those eight rows is exactly the B operand of one 16x16x32 MFMA (column
@@ -138,73 +140,131 @@ __device__ __forceinline__ void load_scales(const uint16_t* p, float (&s)[N]) {
 
 // ------------------------------------------------------------------------------------
 // gate/up + GeGLU: H[row0 + m][n] = fp16(gelu_tanh(s_g[n] * G[m][n]) * (s_u[n] * U[m][n]))
-// grid (f / kSlab, E), block 128: wavefront 0 = gate, wavefront 1 = up.
-template <int MT, int kStages>
+// grid (f / kSlab, parts, E), block 128: wavefront 0 = gate, wavefront 1 = up.
+// kPartial (parts > 1): part p of the contraction writes its unscaled sums to
+// P[(2 p + matrix) * rows_cap + row][n] (fp32) instead; geglu_finish_kernel completes H.
+template <int MT, int kStages, bool kPartial>
 __global__ __launch_bounds__(128) void gate_up_decode_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, const int8_t* __restrict__ w_gate,
     const int8_t* __restrict__ w_up, const uint16_t* __restrict__ scales, _Float16* __restrict__ H,
-    int d, int f) {
-  __shared__ float s_up[MT * 16][kSlab + 4];  // s_u * U of the pass, [row][slab column]
-  const int e = blockIdx.y;
+    float* __restrict__ P, int d, int f, int rows_cap) {
+  __shared__ float s_up[kPartial ? 1 : MT * 16][kSlab + 4];  // s_u * U of the pass, [row][slab column]
+  const int e = blockIdx.z, part = blockIdx.y;
   const int row0 = offsets[e];
   const int M = offsets[e + 1] - row0;
   if (M <= 0) return;
+  const int kspan = d / gridDim.y, kbeg = part * kspan;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wavefront
   const int lane = threadIdx.x & 63, kg = lane >> 4, cl = lane & 15;
   const int nl = kNcol * cl;  // first of the lane's columns within the slab
   const int n0 = blockIdx.x * kSlab + nl;
   const __amdgpu_buffer_rsrc_t wr = weight_rsrc((wave == 0 ? w_gate : w_up) + (size_t)e * d * f, (size_t)d * f);
-  const uint32_t voff = (uint32_t)(8 * kg) * (uint32_t)f + (uint32_t)n0;
+  const uint32_t voff = (uint32_t)(kbeg + 8 * kg) * (uint32_t)f + (uint32_t)n0;
   float s8[kNcol];
-  load_scales<kNcol>(scales + (size_t)e * (2 * (size_t)f + d) + (wave == 0 ? 0 : f) + n0, s8);
+  if constexpr (!kPartial)
+    load_scales<kNcol>(scales + (size_t)e * (2 * (size_t)f + d) + (wave == 0 ? 0 : f) + n0, s8);
 
   for (int pb = 0; pb < M; pb += 16 * MT) {
     const uint16_t* a[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int m = min(pb + 16 * mt + cl, M - 1);
-      a[mt] = x + (size_t)perm[row0 + m] * d + 8 * kg;
+      a[mt] = x + (size_t)perm[row0 + m] * d + kbeg + 8 * kg;
     }
     f32x4 acc[MT][kNcol];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int j = 0; j < kNcol; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    stream_slab<bf16x8, MT, kStages>(wr, voff, (uint32_t)f, d / kStep, a, acc);
+    stream_slab<bf16x8, MT, kStages>(wr, voff, (uint32_t)f, kspan / kStep, a, acc);
 
-    // lane holds rows 16 mt + 4 kg + i of the pass, columns nl .. nl + kNcol - 1 of the slab
-    if (wave == 1) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < kNcol; ++j) s_up[16 * mt + 4 * kg + i][nl + j] = acc[mt][j][i] * s8[j];
-    }
-    __syncthreads();
-    if (wave == 0) {
+    if constexpr (kPartial) {
+      // lane holds rows 16 mt + 4 kg + i of the pass, columns n0 .. n0 + kNcol - 1
+      float* Pp = P + (size_t)(2 * part + wave) * rows_cap * f;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int m = pb + 16 * mt + 4 * kg + i;
           if (m < M) {
-            const float* urow = s_up[16 * mt + 4 * kg + i] + nl;
+            float* dst = Pp + (size_t)(row0 + m) * f + n0;
 #pragma unroll
-            for (int q = 0; q < kNcol / 8; ++q) {
-              uint32_t packed[4];
-#pragma unroll
-              for (int j = 8 * q; j < 8 * q + 8; j += 2)
-                packed[(j >> 1) & 3] = pack_f16_rne(gelu_tanh(acc[mt][j][i] * s8[j]) * urow[j],
-                                                    gelu_tanh(acc[mt][j + 1][i] * s8[j + 1]) * urow[j + 1]);
-              u32x4 v = {packed[0], packed[1], packed[2], packed[3]};
-              *reinterpret_cast<u32x4*>(H + (size_t)(row0 + m) * f + n0 + 8 * q) = v;
-            }
+            for (int q = 0; q < kNcol / 4; ++q)
+              reinterpret_cast<f32x4*>(dst)[q] =
+                  f32x4{acc[mt][4 * q][i], acc[mt][4 * q + 1][i], acc[mt][4 * q + 2][i], acc[mt][4 * q + 3][i]};
           }
         }
+    } else {
+      // lane holds rows 16 mt + 4 kg + i of the pass, columns nl .. nl + kNcol - 1 of the slab
+      if (wave == 1) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < kNcol; ++j) s_up[16 * mt + 4 * kg + i][nl + j] = acc[mt][j][i] * s8[j];
+      }
+      __syncthreads();
+      if (wave == 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = pb + 16 * mt + 4 * kg + i;
+            if (m < M) {
+              const float* urow = s_up[16 * mt + 4 * kg + i] + nl;
+#pragma unroll
+              for (int q = 0; q < kNcol / 8; ++q) {
+                uint32_t packed[4];
+#pragma unroll
+                for (int j = 8 * q; j < 8 * q + 8; j += 2)
+                  packed[(j >> 1) & 3] = pack_f16_rne(gelu_tanh(acc[mt][j][i] * s8[j]) * urow[j],
+                                                      gelu_tanh(acc[mt][j + 1][i] * s8[j + 1]) * urow[j + 1]);
+                u32x4 v = {packed[0], packed[1], packed[2], packed[3]};
+                *reinterpret_cast<u32x4*>(H + (size_t)(row0 + m) * f + n0 + 8 * q) = v;
+              }
+            }
+          }
+      }
+      __syncthreads();  // s_up is rewritten by the next pass
     }
-    __syncthreads();  // s_up is rewritten by the next pass
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// The GeGLU epilogue of a split gate/up contraction: for row r < offsets[E] (expert e),
+// g = s_g * (sum over parts p in order of P[2p][r]), u likewise from P[2p + 1]; H[r] =
+// fp16(gelu_tanh(g) * u). grid (rows_cap), block 256, 8 columns per thread and step.
+__global__ __launch_bounds__(256) void geglu_finish_kernel(const float* __restrict__ P,
+                                                           const int32_t* __restrict__ offsets,
+                                                           const uint16_t* __restrict__ scales,
+                                                           _Float16* __restrict__ H, int parts, int d, int f,
+                                                           int E, int rows_cap) {
+  const int r = blockIdx.x;
+  if (r >= offsets[E]) return;
+  int e = 0;
+  while (e + 1 < E && offsets[e + 1] <= r) ++e;
+  const uint16_t* sc = scales + (size_t)e * (2 * (size_t)f + d);
+  const size_t plane = (size_t)rows_cap * f;
+  for (int n = 8 * threadIdx.x; n < f; n += 8 * 256) {
+    f32x4 g[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    f32x4 u[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    for (int p = 0; p < parts; ++p) {
+      const f32x4* gp = reinterpret_cast<const f32x4*>(P + (2 * p) * plane + (size_t)r * f + n);
+      const f32x4* up = reinterpret_cast<const f32x4*>(P + (2 * p + 1) * plane + (size_t)r * f + n);
+      g[0] += gp[0], g[1] += gp[1];
+      u[0] += up[0], u[1] += up[1];
+    }
+    float sg[8], su[8];
+    load_scales<8>(sc + n, sg);
+    load_scales<8>(sc + f + n, su);
+    uint32_t packed[4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2)
+      packed[j >> 1] = pack_f16_rne(gelu_tanh(g[j >> 2][j & 3] * sg[j]) * (u[j >> 2][j & 3] * su[j]),
+                                    gelu_tanh(g[j >> 2][(j & 3) + 1] * sg[j + 1]) * (u[j >> 2][(j & 3) + 1] * su[j + 1]));
+    *reinterpret_cast<u32x4*>(H + (size_t)r * f + n) = u32x4{packed[0], packed[1], packed[2], packed[3]};
   }
 }
 
@@ -263,15 +323,29 @@ __global__ __launch_bounds__(64) void down_decode_kernel(
 
 hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* perm, const int32_t* offsets,
                                  const int8_t* w_gate, const int8_t* w_up, const uint16_t* scales,
-                                 _Float16* H, int T, int d, int f, int E, hipStream_t stream) {
-  dim3 grid(f / kSlab, E), block(128);
+                                 _Float16* H, float* P, int parts, int T, int k, int d, int f, int E,
+                                 hipStream_t stream) {
+  dim3 grid(f / kSlab, parts, E), block(128);
+  const int rows_cap = T * k;
   // ring depths measured best at the Grok-1 shape (T = 8 and T = 64)
-  if (T <= 16)
-    hipLaunchKernelGGL((gate_up_decode_kernel<1, 4>), grid, block, 0, stream, x, perm, offsets, w_gate, w_up,
-                       scales, H, d, f);
-  else
-    hipLaunchKernelGGL((gate_up_decode_kernel<2, 3>), grid, block, 0, stream, x, perm, offsets, w_gate, w_up,
-                       scales, H, d, f);
+  if (parts > 1) {
+    if (T <= 16)
+      hipLaunchKernelGGL((gate_up_decode_kernel<1, 4, true>), grid, block, 0, stream, x, perm, offsets, w_gate,
+                         w_up, scales, H, P, d, f, rows_cap);
+    else
+      hipLaunchKernelGGL((gate_up_decode_kernel<2, 3, true>), grid, block, 0, stream, x, perm, offsets, w_gate,
+                         w_up, scales, H, P, d, f, rows_cap);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(geglu_finish_kernel, dim3(rows_cap), dim3(256), 0, stream, P, offsets, scales, H, parts, d,
+                       f, E, rows_cap);
+  } else if (T <= 16) {
+    hipLaunchKernelGGL((gate_up_decode_kernel<1, 4, false>), grid, block, 0, stream, x, perm, offsets, w_gate,
+                       w_up, scales, H, P, d, f, rows_cap);
+  } else {
+    hipLaunchKernelGGL((gate_up_decode_kernel<2, 3, false>), grid, block, 0, stream, x, perm, offsets, w_gate,
+                       w_up, scales, H, P, d, f, rows_cap);
+  }
   return hipGetLastError();
 }
 

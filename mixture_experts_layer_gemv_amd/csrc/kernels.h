@@ -23,9 +23,12 @@ hipError_t launch_dispatch(const int32_t* ids, const uint8_t* pad_mask, int32_t*
                            int32_t* offsets, int32_t* perm, int32_t* pos, int T, int E, int k,
                            hipStream_t stream);
 
+// parts > 1: the contraction over d is split in `parts`; P (fp32, 2 * parts * T * k * f
+// elements) holds the partial sums, completed into H by a second launch.
 hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* perm, const int32_t* offsets,
                                  const int8_t* w_gate, const int8_t* w_up, const uint16_t* scales,
-                                 _Float16* H, int T, int d, int f, int E, hipStream_t stream);
+                                 _Float16* H, float* P, int parts, int T, int k, int d, int f, int E,
+                                 hipStream_t stream);
 
 hipError_t launch_down_decode(const _Float16* H, const int32_t* offsets, const int8_t* w_down,
                               const uint16_t* scales, float* Y, int splits, int rows_cap, int T,

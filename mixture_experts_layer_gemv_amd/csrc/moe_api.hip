@@ -57,20 +57,32 @@ int hip_fail(hipError_t e, const char* where) {
     if (_e != hipSuccess) return hip_fail(_e, where); \
   } while (0)
 
-int down_splits(int T, int f) {
+// Decode (T <= 64) splits the contractions when the 256-column slabs alone would leave the
+// chip under-filled: enough parts for about 1024 workgroups, at most 8, each part at least
+// 512 (down) or 768 (gate/up) rows deep and a whole number of 128-row steps.
+constexpr int kFillWorkgroups = 1024;
+
+int down_splits(int T, int d, int f, int E) {
   if (T > moe::kDecodeMaxT) return 1;
-  int s = f / 4096;
-  if (s < 1) s = 1;
-  if (s > 8) s = 8;
-  while (s > 1 && (f / 128) % s != 0) s /= 2;
+  const long slabs = (long)(d / 256) * E;
+  int s = 1;
+  while (s < 8 && slabs * s < kFillWorkgroups && f / (2 * s) >= 512 && (f / 128) % (2 * s) == 0) s *= 2;
+  return s;
+}
+
+int gate_up_parts(int T, int d, int f, int E) {
+  if (T > moe::kDecodeMaxT) return 1;
+  const long slabs = (long)(f / 256) * E;
+  int s = 1;
+  while (s < 8 && slabs * s < kFillWorkgroups && d / (2 * s) >= 768 && (d / 128) % (2 * s) == 0) s *= 2;
   return s;
 }
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
-  size_t ids, w, counts, offsets, perm, pos, h, y, total;
-  int splits;
+  size_t ids, w, counts, offsets, perm, pos, h, y, gp, total;
+  int splits, gparts;
 };
 
 Layout make_layout(int T, int d, int f, int E, int k) {
@@ -89,8 +101,10 @@ Layout make_layout(int T, int d, int f, int E, int k) {
   L.perm = take(tk * 4);
   L.pos = take(tk * 4);
   L.h = take(tk * f * 2);
-  L.splits = down_splits(T, f);
+  L.splits = down_splits(T, d, f, E);
   L.y = take((size_t)L.splits * tk * d * 4);
+  L.gparts = gate_up_parts(T, d, f, E);
+  L.gp = L.gparts > 1 ? take((size_t)2 * L.gparts * tk * f * 4) : 0;
   L.total = at;
   return L;
 }
@@ -169,10 +183,11 @@ int check_layer_args(const void* x, const float* router_w, const int8_t* w_gate,
 
 int run_experts(const uint16_t* x, const int32_t* perm, const int32_t* offsets, const int8_t* w_gate,
                 const int8_t* w_up, const int8_t* w_down, const uint16_t* scales, _Float16* h,
-                float* y, int splits, int T, int d, int f, int E, int k, hipStream_t s) {
+                float* y, int splits, float* gp, int gparts, int T, int d, int f, int E, int k, hipStream_t s) {
   const int rows_cap = T * k;
   if (T <= moe::kDecodeMaxT) {
-    MOE_HIP(moe::launch_gate_up_decode(x, perm, offsets, w_gate, w_up, scales, h, T, d, f, E, s), "gate_up");
+    MOE_HIP(moe::launch_gate_up_decode(x, perm, offsets, w_gate, w_up, scales, h, gp, gparts, T, k, d, f, E, s),
+            "gate_up");
     MOE_HIP(moe::launch_down_decode(h, offsets, w_down, scales, y, splits, rows_cap, T, d, f, E, s), "down");
   } else {
     MOE_HIP(moe::launch_gate_up_prefill(x, perm, offsets, w_gate, w_up, scales, h, rows_cap, d, f, E, s),
@@ -197,7 +212,7 @@ size_t moe_workspace_bytes(int T, int d, int f, int E, int k) {
 
 int moe_down_splits(int T, int d, int f, int E, int k) {
   if (check_shape(T, d, f, E, k) != MOE_OK) return 0;
-  return down_splits(T, f);
+  return down_splits(T, d, f, E);
 }
 
 void moe_release_workspace(void) {
@@ -240,12 +255,13 @@ int moe_forward_ex(const void* x, const float* router_w, const int8_t* w_gate, c
   auto* pos = reinterpret_cast<int32_t*>(ws + L.pos);
   auto* h = reinterpret_cast<_Float16*>(ws + L.h);
   auto* y = reinterpret_cast<float*>(ws + L.y);
+  auto* gp = reinterpret_cast<float*>(ws + L.gp);
   const auto* xb = static_cast<const uint16_t*>(x);
   const auto* sc = static_cast<const uint16_t*>(scales);
 
   MOE_HIP(moe::launch_router(xb, router_w, router_bias, pad_mask, ids, w, T, d, E, k, s), "router");
   MOE_HIP(moe::launch_dispatch(ids, pad_mask, counts, offsets, perm, pos, T, E, k, s), "dispatch");
-  MOE_TRY(run_experts(xb, perm, offsets, w_gate, w_up, w_down, sc, h, y, L.splits, T, d, f, E, k, s));
+  MOE_TRY(run_experts(xb, perm, offsets, w_gate, w_up, w_down, sc, h, y, L.splits, gp, L.gparts, T, d, f, E, k, s));
   MOE_HIP(moe::launch_combine(y, L.splits, (size_t)T * k * d, pos, w, pad_mask, out, T, d, k, s), "combine");
 
   if (dbg) {
@@ -299,12 +315,13 @@ int moe_forward_dense(const void* x, const float* router_w, const int8_t* w_gate
   auto* pos = reinterpret_cast<int32_t*>(in + L.pos);
   auto* h = reinterpret_cast<_Float16*>(in + L.h);
   auto* y = reinterpret_cast<float*>(in + L.y);
+  auto* gp = reinterpret_cast<float*>(in + L.gp);
   const auto* xb = static_cast<const uint16_t*>(x);
   const auto* sc = static_cast<const uint16_t*>(scales);
   MOE_HIP(moe::launch_router(xb, router_w, router_bias, pad_mask, ids, w, T, d, E, k, s), "router");
   MOE_HIP(moe::launch_onehot_expand(ids, w, pad_mask, ids_all, gates, T, E, k, s), "onehot_expand");
   MOE_HIP(moe::launch_dispatch(ids_all, pad_mask, counts, offsets, perm, pos, T, E, E, s), "dispatch");
-  MOE_TRY(run_experts(xb, perm, offsets, w_gate, w_up, w_down, sc, h, y, L.splits, T, d, f, E, E, s));
+  MOE_TRY(run_experts(xb, perm, offsets, w_gate, w_up, w_down, sc, h, y, L.splits, gp, L.gparts, T, d, f, E, E, s));
   MOE_HIP(moe::launch_combine(y, L.splits, (size_t)T * E * d, pos, gates, pad_mask, out, T, d, E, s), "combine");
   return MOE_OK;
 }
@@ -347,12 +364,13 @@ int moe_block_forward(const void* h, const float* norm_pre, const float* norm_po
   auto* pos = reinterpret_cast<int32_t*>(in + L.pos);
   auto* hh = reinterpret_cast<_Float16*>(in + L.h);
   auto* y = reinterpret_cast<float*>(in + L.y);
+  auto* gp = reinterpret_cast<float*>(in + L.gp);
   const auto* hb = static_cast<const uint16_t*>(h);
   const auto* sc = static_cast<const uint16_t*>(scales);
   MOE_HIP(moe::launch_prenorm_router(hb, norm_pre, eps, xn, router_w, router_bias, pad_mask, ids, w, T, d, E, k, s),
           "prenorm_router");
   MOE_HIP(moe::launch_dispatch(ids, pad_mask, counts, offsets, perm, pos, T, E, k, s), "dispatch");
-  MOE_TRY(run_experts(xn, perm, offsets, w_gate, w_up, w_down, sc, hh, y, L.splits, T, d, f, E, k, s));
+  MOE_TRY(run_experts(xn, perm, offsets, w_gate, w_up, w_down, sc, hh, y, L.splits, gp, L.gparts, T, d, f, E, k, s));
   MOE_HIP(moe::launch_combine_postnorm(y, L.splits, (size_t)T * k * d, pos, w, pad_mask, hb, norm_post, eps, h_out,
                                        T, d, k, s),
           "combine_postnorm");
@@ -412,9 +430,16 @@ int moe_gate_up(const void* x, const int32_t* perm, const int32_t* offsets, cons
   const auto* xb = static_cast<const uint16_t*>(x);
   const auto* sc = static_cast<const uint16_t*>(scales);
   auto* hh = static_cast<_Float16*>(h);
-  if (T <= moe::kDecodeMaxT)
-    MOE_HIP(moe::launch_gate_up_decode(xb, perm, offsets, w_gate, w_up, sc, hh, T, d, f, E, s), "gate_up");
-  else
+  if (T <= moe::kDecodeMaxT) {
+    // the same split of the contraction as moe_forward; its partial sums live in the
+    // library workspace
+    const int parts = gate_up_parts(T, d, f, E);
+    char* gp = nullptr;
+    if (parts > 1) MOE_TRY(library_workspace((size_t)2 * parts * T * k * f * 4, &gp));
+    MOE_HIP(moe::launch_gate_up_decode(xb, perm, offsets, w_gate, w_up, sc, hh, reinterpret_cast<float*>(gp), parts,
+                                       T, k, d, f, E, s),
+            "gate_up");
+  } else
     MOE_HIP(moe::launch_gate_up_prefill(xb, perm, offsets, w_gate, w_up, sc, hh, T * k, d, f, E, s), "gate_up");
   return MOE_OK;
 }

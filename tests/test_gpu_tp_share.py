@@ -4,8 +4,10 @@ Guide, section 6: the expert matmuls under shard_map with a psum over the model 
 The layer is split into G shares of f / G columns of gate/up (and rows of down) with all
 experts in each; each share is an ordinary call of the library at the share's shape, and
 the layer's output is the sum of the shares' outputs (the all-reduce, done here on the
-host). At decode the full layer's split-K parts cover the same column ranges as the shares,
-so the sum matches the one-GPU layer up to the rounding of the final fp32 additions."""
+host). Routing is the same on every share; H and the down contraction are summed in other
+orders (a share splits its narrower contraction differently), so an fp32 value of H can
+differ in its last bits and its fp16 rounding flip by one ulp (2^-11 relative): the sum
+matches the one-GPU layer to about 1e-4 of its RMS, where a wrong decomposition is O(1)."""
 from __future__ import annotations
 
 import numpy as np
@@ -24,7 +26,7 @@ if not torch.cuda.is_available():  # pragma: no cover
 import mixture_experts_layer_gemv_amd as moe  # noqa: E402
 from test_gpu_parity import check_layer, workload  # noqa: E402
 
-SUM_TOL = 1e-5  # max|sum of shares - layer| / rms(layer): fp32 rounding only
+SUM_TOL = 1e-3  # max|sum of shares - layer| / rms(layer): summation order and fp16 ulp flips of H
 
 
 def forward(d, T, dd, f, E, k):
