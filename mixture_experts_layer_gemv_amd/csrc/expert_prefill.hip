@@ -11,8 +11,9 @@
 // wavefront on each SIMD covers the other's waits. The contraction runs in 64-deep slices:
 //   * the next slice's activations (16 B per load) and int8 weights (one dword of 4
 //     columns from each of 8 rows per thread and half-tile, through buffer loads whose
-//     row offset is a scalar) are loaded into registers while the current slice's MFMAs
-//     run, then written into the other of two LDS buffers (one barrier per slice);
+//     row offset is a scalar) are loaded into registers two slices ahead and written into
+//     the other of two LDS buffers interleaved with the current slice's MFMAs (one
+//     barrier per slice);
 //   * the weights are converted int8 -> bf16 (gate/up) or fp16 (down) once per
 //     workgroup, on the way into LDS, and stored transposed ([column][k]), so every MFMA
 //     operand is one 16-byte LDS read; column 2 c + q of a 64-column group goes to LDS
@@ -250,21 +251,41 @@ __global__ __launch_bounds__(kThreads) void expert_prefill_kernel(
     }
   };
 
-  // slices it (even) and it + 1 (odd) per trip; nslices is a multiple of 4
+  // Instruction order of one slice plus the next slice's LDS store: every MFMA is followed
+  // by one fragment read, two conversion instructions and one LDS write, so that the store
+  // of the next slice runs in the shadow of this slice's MFMAs instead of after them (the
+  // two wavefronts of a SIMD reach the store phase together, between the same barriers).
+  auto interleave = [&]() {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+    }
+  };
+
+  // slices it (even) and it + 1 (odd) per trip; nslices is a multiple of 4. The loads and
+  // stores are unconditional (past the end they re-read the last slice into a buffer that
+  // is not read again): a conditional load would make the compiler's wait counts at the
+  // stores assume the path without it, i.e. wait for the loads just issued.
   uint16_t* L0 = lds;
   uint16_t* L1 = lds + STAGE_ELEMS;
+  const int klast = (nslices - 1) * BK;
   gload(R0, 0);
-  gload(R1, BK);
+  gload(R1, min(BK, klast));
   lds_store(R0, L0);
   __syncthreads();
   for (int it = 0; it < nslices; it += 2) {
-    if (it + 2 < nslices) gload(R0, (it + 2) * BK);
+    gload(R0, min((it + 2) * BK, klast));
     slice(L0);
     lds_store(R1, L1);
+    interleave();
     __syncthreads();
-    if (it + 3 < nslices) gload(R1, (it + 3) * BK);
+    gload(R1, min((it + 3) * BK, klast));
     slice(L1);
-    if (it + 2 < nslices) lds_store(R0, L0);
+    lds_store(R0, L0);
+    interleave();
     __syncthreads();
   }
 
