@@ -19,6 +19,8 @@ import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
+# the launch policy (split counts, tile orders) that the kernels run under
+POLICY_SOURCE = "mixture_experts_layer_gemv_amd/csrc/moe_api.hip"
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s; % HBM peak (decode T<=64), % MFMA peak (prefill)"
@@ -57,20 +59,24 @@ def algorithmic_work(spec, counts):
 def recorded_traffic(workload: str, source: str):
     """HBM traffic of the gate/up kernel as measured by rocprofv3 FETCH_SIZE / WRITE_SIZE
     (scaled by the copy calibration) and recorded in profiles/, or None when no record
-    matches this workload and the current kernel source (the counters are void once the
-    kernel changes)."""
+    matches this workload, the current kernel source and the current launch policy (the
+    counters are void once either changes)."""
     import glob
     import hashlib
     import re
 
+    files = [source, POLICY_SOURCE]
     try:
-        digest = hashlib.sha256(open(os.path.join(ROOT, source), "rb").read()).hexdigest()[:16]
+        h = hashlib.sha256()
+        for rel in files:
+            h.update(open(os.path.join(ROOT, rel), "rb").read())
+        digest = h.hexdigest()[:16]
     except OSError:
         return None
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         for m in re.finditer(r"<!-- traffic-record (\{.*?\}) -->", open(path).read()):
             rec = json.loads(m.group(1))
-            if rec.get("workload") == workload and rec.get("source") == source and rec.get("source_sha256_16") == digest:
+            if rec.get("workload") == workload and rec.get("sources") == files and rec.get("sources_sha256_16") == digest:
                 rec["profile"] = os.path.relpath(path, ROOT)
                 return rec
     return None

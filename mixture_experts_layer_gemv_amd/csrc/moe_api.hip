@@ -58,9 +58,10 @@ int hip_fail(hipError_t e, const char* where) {
   } while (0)
 
 // Decode (T <= 64) splits the contractions when the 256-column slabs alone would leave the
-// chip under-filled: enough parts for about 1024 workgroups, at most 8, each part at least
+// chip under-filled: enough parts for about 512 workgroups (measured better than 1024: longer
+// streams per wavefront), at most 8, each part at least
 // 512 (down) or 768 (gate/up) rows deep and a whole number of 128-row steps.
-constexpr int kFillWorkgroups = 1024;
+constexpr int kFillWorkgroups = 512;
 
 int down_splits(int T, int d, int f, int E) {
   if (T > moe::kDecodeMaxT) return 1;

@@ -21,8 +21,9 @@ if not torch.cuda.is_available():  # pragma: no cover - collected on CPU, skippe
 
 import mixture_experts_layer_gemv_amd as moe  # noqa: E402
 
-CONFIG_NAMES = ["tiny", "decode", "batched_decode", "prefill", "skewed"]
-SAMPLE = {"tiny": 64, "decode": 8, "batched_decode": 16, "prefill": 16, "skewed": 16}
+CONFIG_NAMES = ["tiny", "decode", "batched_decode", "prefill", "skewed", "decode_tp8", "prefill_tp8"]
+SAMPLE = {"tiny": 64, "decode": 8, "batched_decode": 16, "prefill": 16, "skewed": 16, "decode_tp8": 8,
+          "prefill_tp8": 16}
 
 _cache: dict = {}
 
