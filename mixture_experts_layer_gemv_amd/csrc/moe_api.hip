@@ -58,16 +58,18 @@ int hip_fail(hipError_t e, const char* where) {
   } while (0)
 
 // Decode (T <= 64) splits the contractions when the 256-column slabs alone would leave the
-// chip under-filled: enough parts for about 512 workgroups (measured better than 1024: longer
-// streams per wavefront), at most 8, each part at least
-// 512 (down) or 768 (gate/up) rows deep and a whole number of 128-row steps.
-constexpr int kFillWorkgroups = 512;
-
+// chip under-filled. Targets measured on whole forward passes at the Grok-1 shape and at one
+// GPU's tensor-parallel share: the down projection wants about 1024 workgroups while each
+// wavefront carries one 16-row tile (T <= 16) and about 512 with two (longer streams win
+// once the MFMA work per byte doubles), with parts of at least 1024 rows (shorter ones lose
+// to their start-up); gate/up wants about 512 workgroups with parts of at least 768 rows.
+// At most 8 parts, each a whole number of 128-row steps.
 int down_splits(int T, int d, int f, int E) {
   if (T > moe::kDecodeMaxT) return 1;
   const long slabs = (long)(d / 256) * E;
+  const long target = T <= 16 ? 1024 : 512;
   int s = 1;
-  while (s < 8 && slabs * s < kFillWorkgroups && f / (2 * s) >= 512 && (f / 128) % (2 * s) == 0) s *= 2;
+  while (s < 8 && slabs * s < target && f / (2 * s) >= 1024 && (f / 128) % (2 * s) == 0) s *= 2;
   return s;
 }
 
@@ -75,7 +77,7 @@ int gate_up_parts(int T, int d, int f, int E) {
   if (T > moe::kDecodeMaxT) return 1;
   const long slabs = (long)(f / 256) * E;
   int s = 1;
-  while (s < 8 && slabs * s < kFillWorkgroups && d / (2 * s) >= 768 && (d / 128) % (2 * s) == 0) s *= 2;
+  while (s < 8 && slabs * s < 512 && d / (2 * s) >= 768 && (d / 128) % (2 * s) == 0) s *= 2;
   return s;
 }
 

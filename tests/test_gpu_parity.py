@@ -295,7 +295,7 @@ def small_case(name, **kw):
     dict(T=33, d=768, f=1024, E=8, k=2, x_dist="student4"),
     dict(T=1000, d=256, f=768, E=8, k=2, bias=(3.0, 2.0, 0, 0, 0, 0, 0, 0)),
     # narrow f at decode: the gate/up contraction split in 2 (one 16-row tile) or 4 parts
-    # (two tiles, padded), the down contraction split in 4
+    # (two tiles, padded), the down contraction split in 2
     dict(T=8, d=3072, f=1024, E=8, k=2, scale_jitter=True),
     dict(T=40, d=6144, f=512, E=8, k=2, n_pad=4),
     dict(T=8, d=1536, f=2048, E=8, k=2, x_dist="student4"),
