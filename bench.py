@@ -112,7 +112,7 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode",
                     choices=["tiny", "decode", "batched_decode", "prefill", "skewed", "decode_tp8", "prefill_tp8"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -186,6 +186,48 @@ def main() -> int:
                                   router_bias=bias)
     step()
     torch.cuda.synchronize()
+    gu_ms = dn_ms = None
+    if args.variant == "gather":
+        # ---- per-kernel durations (first, so that the GPU is at its steady clocks for the timed
+        #      steps after it): the same kernels through the stage entry points, with HIP events
+        #      recorded on the launch stream around the two expert kernels
+        tk = T * k
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+        offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        perm = torch.empty(max(tk, 1), dtype=torch.int32, device=dev)
+        pos = torch.empty((T, k), dtype=torch.int32, device=dev)
+        h = torch.empty((tk, f), dtype=torch.float16, device=dev)
+        splits = moe.down_splits(T, d, f, E, k)
+        y = torch.empty((splits, tk, d), dtype=torch.float32, device=dev)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+        def staged(e=None):
+            moe.moe_route(x, wr, bias, pad, ids, wts, T, d, E, k, stream)
+            moe.moe_dispatch(ids, pad, counts_t, offsets, perm, pos, T, E, k, stream)
+            if e:
+                e[0].record(stream)
+            moe.moe_gate_up(x, perm, offsets, wg, wu, sc, h, T, d, f, E, k, stream)
+            if e:
+                e[1].record(stream)
+                e[2].record(stream)
+            moe.moe_down(h, offsets, wd, sc, y, splits, T, d, f, E, k, stream)
+            if e:
+                e[3].record(stream)
+            moe.moe_combine(y, splits, pos, wts, pad, out, T, d, k, stream)
+
+        # from idle the GPU takes ~15 ms of work to reach its steady clocks: warm the staged
+        # passes up for at least 20 of them
+        for _ in range(max(20, args.warmup)):
+            staged()
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            staged(evs[i])
+        torch.cuda.synchronize()
+        gu_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+        dn_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+        log(f"gate_up {gu_ms:.4f} ms, down {dn_ms:.4f} ms (splits={splits})")
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -208,43 +250,6 @@ def main() -> int:
                           "config": {"workload": f"{args.workload}: {spec.description}", "T": T, "d": d, "f": f,
                                      "E": E, "k": k, "n_pad": spec.n_pad}}), flush=True)
         return 0
-
-    # ---- per-kernel durations: the same kernels through the stage entry points, with HIP
-    #      events recorded on the launch stream around the two expert kernels
-    tk = T * k
-    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-    wts = torch.empty((T, k), dtype=torch.float32, device=dev)
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    perm = torch.empty(max(tk, 1), dtype=torch.int32, device=dev)
-    pos = torch.empty((T, k), dtype=torch.int32, device=dev)
-    h = torch.empty((tk, f), dtype=torch.float16, device=dev)
-    splits = moe.down_splits(T, d, f, E, k)
-    y = torch.empty((splits, tk, d), dtype=torch.float32, device=dev)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-
-    def staged(e=None):
-        moe.moe_route(x, wr, bias, pad, ids, wts, T, d, E, k, stream)
-        moe.moe_dispatch(ids, pad, counts_t, offsets, perm, pos, T, E, k, stream)
-        if e:
-            e[0].record(stream)
-        moe.moe_gate_up(x, perm, offsets, wg, wu, sc, h, T, d, f, E, k, stream)
-        if e:
-            e[1].record(stream)
-            e[2].record(stream)
-        moe.moe_down(h, offsets, wd, sc, y, splits, T, d, f, E, k, stream)
-        if e:
-            e[3].record(stream)
-        moe.moe_combine(y, splits, pos, wts, pad, out, T, d, k, stream)
-
-    for _ in range(max(1, args.warmup)):
-        staged()
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        staged(evs[i])
-    torch.cuda.synchronize()
-    gu_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    dn_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
-    log(f"gate_up {gu_ms:.4f} ms, down {dn_ms:.4f} ms (splits={splits})")
 
     work = algorithmic_work(spec, counts)
     decode = T <= 64
