@@ -41,8 +41,9 @@
  *     moe_last_error() (per thread). Errors:
  *       MOE_ERR_INVALID      a required pointer is NULL or misaligned; T < 0;
  *                            d, f, E or k <= 0; k > E; a workspace that is too small
- *       MOE_ERR_UNSUPPORTED  E > 64; d or f not a multiple of 256; T * max(d, f) * k
- *                            too large for 32-bit row indexing
+ *       MOE_ERR_UNSUPPORTED  E > 64; d or f not a multiple of 256; T * k above 2^24
+ *                            assignments; d * f of 2^31 bytes or more (one expert's
+ *                            matrix is addressed with 32-bit byte offsets)
  *       MOE_ERR_HIP          a HIP launch or copy failed (message holds HIP's string)
  *       MOE_ERR_NOMEM        the library workspace could not be allocated
  *     T == 0 is a successful no-op. Device faults surface at the caller's next sync.

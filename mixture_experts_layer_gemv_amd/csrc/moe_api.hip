@@ -32,6 +32,8 @@ int check_shape(int T, int d, int f, int E, int k) {
   if (E > 64) return fail(MOE_ERR_UNSUPPORTED, "E > 64 is not supported");
   if (d % 256 != 0 || f % 256 != 0) return fail(MOE_ERR_UNSUPPORTED, "d and f must be multiples of 256");
   if ((long long)T * k > kMaxAssignments) return fail(MOE_ERR_UNSUPPORTED, "T * k exceeds 2^24 assignments");
+  // one expert's weight matrix is addressed with 32-bit byte offsets (buffer loads)
+  if ((long long)d * f >= (1ll << 31)) return fail(MOE_ERR_UNSUPPORTED, "d * f must be below 2^31 bytes per matrix");
   return MOE_OK;
 }
 

@@ -62,6 +62,8 @@ def rc_forward(**kw):
     (dict(d=200), moe.MOE_ERR_UNSUPPORTED, "multiples of 256"),
     (dict(f=320), moe.MOE_ERR_UNSUPPORTED, "multiples of 256"),
     (dict(T=1 << 24, k=2), moe.MOE_ERR_UNSUPPORTED, "2^24"),
+    # one expert's matrix must stay below 2^31 bytes (32-bit offsets of the weight loads)
+    (dict(d=65536, f=32768), moe.MOE_ERR_UNSUPPORTED, "2^31"),
 ])
 def test_invalid_arguments_are_rejected_before_any_launch(kw, status, msg):
     assert rc_forward(**kw) == status
@@ -101,6 +103,7 @@ def test_workspace_size_and_split_policy():
     need = moe.workspace_bytes(8, 6144, 32768, 8, 2)
     assert need >= tk * 32768 * 2 + 8 * tk * 6144 * 4
     assert moe.workspace_bytes(0, 6144, 32768, 8, 2) == 0
+    assert moe.workspace_bytes(8, 65536, 32768, 8, 2) == 0  # unsupported shape
     assert moe.workspace_bytes(8, 6144, 32768, 8, 9) == 0
 
 
