@@ -19,8 +19,8 @@ import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-# the launch policy (split counts, tile orders) that the kernels run under
-POLICY_SOURCE = "mixture_experts_layer_gemv_amd/csrc/moe_api.hip"
+# the launch policy (decode split counts) that the kernels run under
+POLICY_SOURCE = "mixture_experts_layer_gemv_amd/csrc/launch_policy.h"
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s; % HBM peak (decode T<=64), % MFMA peak (prefill)"

@@ -1,0 +1,34 @@
+// Launch policy of the decode expert kernels (T <= 64): how many parts the contractions are
+// split into. The kernels stream each touched expert's weights once; a split only adds
+// wavefronts (and fp32 partial sums) when the 256-column slabs alone would leave the chip
+// under-filled, e.g. at one GPU's share of a tensor-parallel split over f.
+#pragma once
+
+#include "kernels.h"
+
+namespace moe {
+
+// Targets measured on whole forward passes at the Grok-1 shape and at one GPU's
+// tensor-parallel share: the down projection wants about 1024 workgroups while each
+// wavefront carries one 16-row tile (T <= 16) and about 512 with two (longer streams win
+// once the MFMA work per byte doubles), with parts of at least 1024 rows (shorter ones lose
+// to their start-up). At most 8 parts, each a whole number of 128-row steps.
+inline int down_splits(int T, int d, int f, int E) {
+  if (T > kDecodeMaxT) return 1;
+  const long slabs = (long)(d / 256) * E;
+  const long target = T <= 16 ? 1024 : 512;
+  int s = 1;
+  while (s < 8 && slabs * s < target && f / (2 * s) >= 1024 && (f / 128) % (2 * s) == 0) s *= 2;
+  return s;
+}
+
+// gate/up: about 512 workgroups, parts of at least 768 rows of the contraction over d.
+inline int gate_up_parts(int T, int d, int f, int E) {
+  if (T > kDecodeMaxT) return 1;
+  const long slabs = (long)(f / 256) * E;
+  int s = 1;
+  while (s < 8 && slabs * s < 512 && d / (2 * s) >= 768 && (d / 128) % (2 * s) == 0) s *= 2;
+  return s;
+}
+
+}  // namespace moe

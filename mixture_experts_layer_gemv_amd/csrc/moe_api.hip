@@ -11,8 +11,12 @@
 
 #include "../../include/moe.h"
 #include "kernels.h"
+#include "launch_policy.h"
 
 namespace {
+
+using moe::down_splits;
+using moe::gate_up_parts;
 
 thread_local std::string g_error;
 
@@ -58,30 +62,6 @@ int hip_fail(hipError_t e, const char* where) {
     hipError_t _e = (expr);                      \
     if (_e != hipSuccess) return hip_fail(_e, where); \
   } while (0)
-
-// Decode (T <= 64) splits the contractions when the 256-column slabs alone would leave the
-// chip under-filled. Targets measured on whole forward passes at the Grok-1 shape and at one
-// GPU's tensor-parallel share: the down projection wants about 1024 workgroups while each
-// wavefront carries one 16-row tile (T <= 16) and about 512 with two (longer streams win
-// once the MFMA work per byte doubles), with parts of at least 1024 rows (shorter ones lose
-// to their start-up); gate/up wants about 512 workgroups with parts of at least 768 rows.
-// At most 8 parts, each a whole number of 128-row steps.
-int down_splits(int T, int d, int f, int E) {
-  if (T > moe::kDecodeMaxT) return 1;
-  const long slabs = (long)(d / 256) * E;
-  const long target = T <= 16 ? 1024 : 512;
-  int s = 1;
-  while (s < 8 && slabs * s < target && f / (2 * s) >= 1024 && (f / 128) % (2 * s) == 0) s *= 2;
-  return s;
-}
-
-int gate_up_parts(int T, int d, int f, int E) {
-  if (T > moe::kDecodeMaxT) return 1;
-  const long slabs = (long)(f / 256) * E;
-  int s = 1;
-  while (s < 8 && slabs * s < 512 && d / (2 * s) >= 768 && (d / 128) % (2 * s) == 0) s *= 2;
-  return s;
-}
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
