@@ -62,6 +62,9 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden symbol visibility; these declarations are its exports. */
+#pragma GCC visibility push(default)
+
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID = 1,
@@ -171,10 +174,11 @@ size_t moe_workspace_bytes_block(int T, int d, int f, int E, int k);
    expert and combine launches of one moe_forward_ex call are captured once into a HIP
    graph; each moe_graph_launch replays all of them with one hipGraphLaunch on `stream`.
    The graph holds the pointers and shapes given here: every replay reads the inputs'
-   current contents at those addresses and writes out. The workspace (caller's, or the
-   library's, allocated here before the capture) must stay alive and must not be used by
-   overlapping calls. moe_graph_create synchronises nothing but may allocate the library
-   workspace; moe_graph_launch allocates nothing. T must be > 0. */
+   current contents at those addresses and writes out. A caller workspace must stay alive
+   as long as the graph and must not be used by overlapping calls; with workspace NULL the
+   graph allocates its own (moe_graph_create may return MOE_ERR_NOMEM) and
+   moe_graph_destroy frees it after waiting for the device. moe_graph_launch allocates
+   nothing; replays of one graph must not overlap. T must be > 0. */
 typedef struct moe_graph moe_graph;
 int moe_graph_create(moe_graph** graph, const void* x, const float* router_w, const int8_t* w_gate,
                      const int8_t* w_up, const int8_t* w_down, const void* scales,
@@ -195,6 +199,8 @@ const char* moe_last_error(void);
 /* ABI version of this header. */
 int moe_abi_version(void);
 #define MOE_ABI_VERSION 1
+
+#pragma GCC visibility pop
 
 #ifdef __cplusplus
 }

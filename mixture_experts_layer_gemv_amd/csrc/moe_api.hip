@@ -184,6 +184,25 @@ int run_experts(const uint16_t* x, const int32_t* perm, const int32_t* offsets, 
 
 }  // namespace
 
+// A captured forward (declared opaque in include/moe.h).
+struct moe_graph {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  void* own_ws = nullptr;  // the graph's own workspace when the caller passed none
+};
+
+namespace {
+void destroy_graph(moe_graph* g) {
+  if (g->exec) (void)hipGraphExecDestroy(g->exec);
+  if (g->graph) (void)hipGraphDestroy(g->graph);
+  if (g->own_ws) {
+    (void)hipDeviceSynchronize();  // a replay may still be running
+    (void)hipFree(g->own_ws);
+  }
+  delete g;
+}
+}  // namespace
+
 extern "C" {
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }
@@ -467,10 +486,6 @@ int moe_combine(const float* y, int splits, const int32_t* pos, const float* top
 // ---------------------------------------------------------------------------------------
 // Single-launch forward: the five launches captured once into a HIP graph and replayed.
 
-struct moe_graph {
-  hipGraph_t graph = nullptr;
-  hipGraphExec_t exec = nullptr;
-};
 
 int moe_graph_create(moe_graph** out_graph, const void* x, const float* router_w, const int8_t* w_gate,
                      const int8_t* w_up, const int8_t* w_down, const void* scales, const uint8_t* pad_mask,
@@ -480,17 +495,32 @@ int moe_graph_create(moe_graph** out_graph, const void* x, const float* router_w
   *out_graph = nullptr;
   MOE_TRY(check_layer_args(x, router_w, w_gate, w_up, w_down, scales, out, T, d, f, E, k));
   if (T == 0) return fail(MOE_ERR_INVALID, "T must be > 0 for a graph");
-  // the workspace must exist before capture: nothing may allocate inside it
+  // The workspace must exist before the capture (nothing may allocate inside it) and must
+  // live as long as the graph: without a caller workspace the graph allocates its own (the
+  // library workspace could be reallocated by a later, larger call).
   char* ws = static_cast<char*>(workspace);
   const size_t need = make_layout(T, d, f, E, k).total;
-  if (!ws) {
-    MOE_TRY(library_workspace(need, &ws));
-  } else if (workspace_bytes < need) {
+  if (ws && workspace_bytes < need)
     return fail(MOE_ERR_INVALID, "workspace too small: need " + std::to_string(need) + " bytes");
+  auto* g = new moe_graph();
+  if (!ws) {
+    const char* hook = std::getenv("MOE_TEST_FAIL_ALLOC");
+    hipError_t ea = (hook && hook[0] == '1') ? hipErrorOutOfMemory : hipMalloc(&g->own_ws, round_up(need, 256));
+    if (ea != hipSuccess) {
+      (void)hipGetLastError();
+      g->own_ws = nullptr;
+      destroy_graph(g);
+      return fail(MOE_ERR_NOMEM, std::string("graph workspace hipMalloc of ") + std::to_string(need) +
+                                     " bytes failed: " + hipGetErrorString(ea));
+    }
+    ws = static_cast<char*>(g->own_ws);
   }
   hipStream_t cs = nullptr;
-  MOE_HIP(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking), "hipStreamCreate");
-  auto* g = new moe_graph();
+  hipError_t ec = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+  if (ec != hipSuccess) {
+    destroy_graph(g);
+    return hip_fail(ec, "hipStreamCreate");
+  }
   int rc = MOE_OK;
   hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
   if (e != hipSuccess) {
@@ -507,9 +537,7 @@ int moe_graph_create(moe_graph** out_graph, const void* x, const float* router_w
   }
   (void)hipStreamDestroy(cs);
   if (rc != MOE_OK) {
-    if (g->exec) (void)hipGraphExecDestroy(g->exec);
-    if (g->graph) (void)hipGraphDestroy(g->graph);
-    delete g;
+    destroy_graph(g);
     return rc;
   }
   *out_graph = g;
@@ -524,9 +552,7 @@ int moe_graph_launch(moe_graph* g, void* stream) {
 
 void moe_graph_destroy(moe_graph* g) {
   if (!g) return;
-  if (g->exec) (void)hipGraphExecDestroy(g->exec);
-  if (g->graph) (void)hipGraphDestroy(g->graph);
-  delete g;
+  destroy_graph(g);
 }
 
 }  // extern "C"

@@ -96,6 +96,24 @@ def test_graph_replays_match_eager(case):
         g.close()
 
 
+def test_graph_without_workspace_owns_its_workspace():
+    # a graph created without a caller workspace keeps its own: a later, larger call that
+    # grows the library workspace (freeing the old buffer) must not affect its replays
+    s, inp, d = small("graph_own", T=48, d=256, f=512, n_pad=3)
+    out = torch.full((s.T, s.d), float("nan"), device="cuda")
+    g = moe.Graph(d["x"], d["router_w"], d["w_gate"], d["w_up"], d["w_down"], d["scales"], d["pad_mask"], out, s.T,
+                  s.d, s.f, s.E, s.k, router_bias=d["router_bias"])
+    try:
+        big, _, dbig = small("graph_big", T=3000, d=512, f=1024)
+        sparse_out(dbig, big)  # grows the library workspace
+        for _ in range(2):
+            g.launch()
+            torch.cuda.synchronize()
+            assert np.array_equal(out.cpu().numpy(), sparse_out(d, s))
+    finally:
+        g.close()
+
+
 # ------------------------------------------------------------------------ MoE block with fused norms
 
 def block_case(s, inp, d, rows):
