@@ -305,6 +305,18 @@ def test_layer_edge_shapes(kw):
     check_layer(inp, d, label=str(kw))
 
 
+@pytest.mark.slow
+def test_layer_at_the_assignment_limit():
+    # T * k = 2^24, the largest batch the library accepts: every index past 32-bit element
+    # counts (x, H, Y, out all exceed 2^31 bytes) and the single-workgroup dispatch over 16.8M
+    # assignments; routing and dispatch checked for every token, the output on sampled rows
+    T = 1 << 23
+    inp, d = small_case("limit", T=T, d=256, f=256, n_pad=1000)
+    pads = np.nonzero(inp["pad_mask"] == 0)[0][:2]
+    rows = sample_rows(T, 24, seed=3, must=np.concatenate([pads, [0, T - 1]]))
+    check_layer(inp, d, rows=rows, label="T=2^23 k=2 d=256 f=256")
+
+
 def test_all_tokens_padded():
     inp, d = small_case("allpad", T=32, d=256, f=512, n_pad=32)
     out, dbg = run_forward(d, 32, 256, 512, 8, 2)
