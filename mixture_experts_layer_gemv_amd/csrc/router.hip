@@ -180,9 +180,117 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(const uint16_t* _
   }
 }
 
+// Large batches, E == 8: one workgroup per TPW tokens, so that each router_w load (the 8
+// rows x 8 experts of a thread's features) serves TPW tokens instead of one. Each token's
+// sums are formed in exactly the order of router_topk_kernel (thread partials over the
+// feature chunks in order, butterfly per wavefront, wavefronts in index order), so a token
+// gets bit-identical logits whatever kernel and batch size route it. Lane j < TPW of
+// wavefront 0 finishes token j.
+template <int TPW>
+__global__ __launch_bounds__(kThreads) void router_topk_multi_kernel(const uint16_t* __restrict__ x,
+                                                                     const float* __restrict__ router_w,
+                                                                     const float* __restrict__ router_bias,
+                                                                     const uint8_t* __restrict__ pad_mask,
+                                                                     int32_t* __restrict__ topk_ids,
+                                                                     float* __restrict__ topk_w, int T, int d,
+                                                                     int k) {
+  constexpr int E = 8;
+  __shared__ float s_part[kWaves][TPW][E];
+  const int t0 = blockIdx.x * TPW;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ntok = min(TPW, T - t0);
+
+  float acc[TPW][E];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j)
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[j][e] = 0.0f;
+
+  for (int i0 = tid * 8; i0 < d; i0 += kThreads * 8) {
+    const f32x4* rw = reinterpret_cast<const f32x4*>(router_w + (size_t)i0 * 8);
+    f32x4 w[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) w[q] = rw[q];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int t = t0 + min(j, ntok - 1);  // past the batch end: a live row, result unused
+      const u32x4 xv = *reinterpret_cast<const u32x4*>(x + (size_t)t * d + i0);
+      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float xf = __uint_as_float((r & 1) ? (xw[r >> 1] & 0xFFFF0000u) : (xw[r >> 1] << 16));
+        const f32x4 lo = w[2 * r], hi = w[2 * r + 1];
+        acc[j][0] += xf * lo.x, acc[j][1] += xf * lo.y, acc[j][2] += xf * lo.z, acc[j][3] += xf * lo.w;
+        acc[j][4] += xf * hi.x, acc[j][5] += xf * hi.y, acc[j][6] += xf * hi.z, acc[j][7] += xf * hi.w;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < TPW; ++j)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float v = acc[j][e];
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+      if (lane == 0) s_part[wave][j][e] = v;
+    }
+  __syncthreads();
+  if (wave != 0 || lane >= ntok) return;
+
+  const int t = t0 + lane;
+  const bool real = pad_mask == nullptr || pad_mask[t] != 0;
+  if (!real) {
+    for (int j = 0; j < k; ++j) {
+      topk_ids[(size_t)t * k + j] = -1;
+      topk_w[(size_t)t * k + j] = 0.0f;
+    }
+    return;
+  }
+  float p[E];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    float v = s_part[0][lane][e];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) v += s_part[w][lane][e];
+    if (router_bias) v += router_bias[e];
+    p[e] = v;
+    mx = fmaxf(mx, v);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    p[e] = expf(p[e] - mx);
+    s += p[e];
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) p[e] = p[e] / s;
+  // k rounds of "largest not yet taken" (strict >, so the lower index wins ties)
+  uint32_t taken = 0;
+  for (int j = 0; j < k; ++j) {
+    int best = -1;
+    float bp = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (!((taken >> e) & 1u) && (best < 0 || p[e] > bp)) {
+        best = e;
+        bp = p[e];
+      }
+    taken |= 1u << best;
+    topk_ids[(size_t)t * k + j] = best;
+    topk_w[(size_t)t * k + j] = bp;
+  }
+}
+
 hipError_t launch_router(const uint16_t* x, const float* router_w, const float* router_bias,
                          const uint8_t* pad_mask, int32_t* topk_ids, float* topk_w, int T, int d,
                          int E, int k, hipStream_t stream) {
+  constexpr int kTPW = 8;  // tokens per workgroup of the large-batch kernel
+  if (E == 8 && T >= 1024) {
+    hipLaunchKernelGGL(router_topk_multi_kernel<kTPW>, dim3((T + kTPW - 1) / kTPW), dim3(kThreads), 0, stream, x,
+                       router_w, router_bias, pad_mask, topk_ids, topk_w, T, d, k);
+    return hipGetLastError();
+  }
   dim3 grid(T), block(kThreads);
   if (E <= 8)
     hipLaunchKernelGGL((router_topk_kernel<8, false>), grid, block, 0, stream, x, router_w, router_bias, pad_mask,

@@ -115,6 +115,28 @@ def check_layer(inp: dict, d: dict, rows=None, label=""):
 
 # ------------------------------------------------------------------------------ routing
 
+def test_router_is_batch_invariant_bitwise():
+    # large batches route 8 tokens per workgroup, small ones one: the same token must get the
+    # same ids and weights bit for bit either way (ragged last group included)
+    s = synth.custom("router_batches", T=1027, d=512, f=256, n_pad=9, bias=(0.5, 0, 0, 0, 0, 0, 0, -0.5))
+    inp = synth.make_inputs(s, with_weights=False)
+    d = to_dev(inp, with_weights=False)
+    ids = torch.empty((s.T, s.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((s.T, s.k), dtype=torch.float32, device="cuda")
+    moe.moe_route(d["x"], d["router_w"], d["router_bias"], d["pad_mask"], ids, w, s.T, s.d, s.E, s.k)
+    ids_b = torch.empty_like(ids)
+    w_b = torch.empty_like(w)
+    for a in range(0, s.T, 300):
+        b = min(s.T, a + 300)
+        moe.moe_route(d["x"][a:b], d["router_w"], d["router_bias"], d["pad_mask"][a:b], ids_b[a:b], w_b[a:b],
+                      b - a, s.d, s.E, s.k)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids_b) and torch.equal(w, w_b)
+    r = oracle.route(inp["x"], inp["router_w"], inp["router_bias"], inp["pad_mask"], s.k)
+    excl, amb = exclusions(r)
+    compare_ids(ids.cpu().numpy(), r["ids"], excl, amb)
+
+
 @pytest.mark.parametrize("name", CONFIG_NAMES)
 def test_route_parity(name):
     inp, d = workload(name)
