@@ -75,7 +75,39 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(const uint16_t* _
     }
     rnorm = 1.0f / sqrtf(block_sum(ss, s_red) / (float)d + eps);
   }
-  for (int i0 = tid * 8; i0 < d; i0 += kThreads * 8) {
+  // acc += the 8 features of x chunk xv against their 8 router_w rows (E == 8)
+  auto accumulate8 = [&](const u32x4& xv, const f32x4 (&w)[16]) {
+    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const float xf = __uint_as_float((r & 1) ? (xw[r >> 1] & 0xFFFF0000u) : (xw[r >> 1] << 16));
+      const f32x4 lo = w[2 * r], hi = w[2 * r + 1];
+      acc[0] += xf * lo.x, acc[1] += xf * lo.y, acc[2] += xf * lo.z, acc[3] += xf * lo.w;
+      acc[4] += xf * hi.x, acc[5] += xf * hi.y, acc[6] += xf * hi.z, acc[7] += xf * hi.w;
+    }
+  };
+  // Up to 3 chunks per thread (d <= 6144), E == 8: every chunk's loads go out before the first
+  // FMA (one memory round trip instead of one per chunk); the sums keep the chunk order.
+  constexpr int kPrefetch = 3;
+  const bool prefetched = !kNorm && EMAX == 8 && E == 8 && d <= kPrefetch * kThreads * 8;
+  if (prefetched) {
+    u32x4 xv[kPrefetch];
+    f32x4 w[kPrefetch][16];
+#pragma unroll
+    for (int s = 0; s < kPrefetch; ++s) {
+      const int i0 = tid * 8 + s * kThreads * 8;
+      if (i0 < d) {
+        xv[s] = *reinterpret_cast<const u32x4*>(xt + i0);
+        const f32x4* rw = reinterpret_cast<const f32x4*>(router_w + (size_t)i0 * 8);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) w[s][q] = rw[q];
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < kPrefetch; ++s)
+      if (tid * 8 + s * kThreads * 8 < d) accumulate8(xv[s], w[s]);
+  }
+  for (int i0 = tid * 8; !prefetched && i0 < d; i0 += kThreads * 8) {
     u32x4 xv = *reinterpret_cast<const u32x4*>(xt + i0);
     uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
     if constexpr (kNorm) {
@@ -96,13 +128,7 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(const uint16_t* _
       f32x4 w[16];
 #pragma unroll
       for (int q = 0; q < 16; ++q) w[q] = rw[q];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const float xf = __uint_as_float((r & 1) ? (xw[r >> 1] & 0xFFFF0000u) : (xw[r >> 1] << 16));
-        const f32x4 lo = w[2 * r], hi = w[2 * r + 1];
-        acc[0] += xf * lo.x, acc[1] += xf * lo.y, acc[2] += xf * lo.z, acc[3] += xf * lo.w;
-        acc[4] += xf * hi.x, acc[5] += xf * hi.y, acc[6] += xf * hi.z, acc[7] += xf * hi.w;
-      }
+      accumulate8(u32x4{xw[0], xw[1], xw[2], xw[3]}, w);
     } else {
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
