@@ -1,9 +1,10 @@
 // Router: fp32 logits, softmax and top-k selection (Grok-1 Admin & Architecture Guide,
 // section 3 "Mixture of Experts", steps 1-2; routing and softmax in fp32, section 9).
 //
-// One workgroup of 256 threads per token. Thread i takes the 8 input features
-// 8 i + 2048 s .. + 7 (s = 0, 1, ...): one 16-byte load of x and the 8 matching rows of
-// router_w (8 E contiguous floats), all issued before use. Partial logits are reduced by
+// One workgroup of 256 threads per token (small batches; large batches with E = 8 take
+// router_topk_multi_kernel, 8 tokens per workgroup, same arithmetic). Thread i takes the 8
+// input features 8 i + 2048 s .. + 7 (s = 0, 1, ...): one 16-byte load of x and the 8
+// matching rows of router_w (8 E contiguous floats), all issued before use. Partial logits are reduced by
 // a butterfly over each wavefront (the xor pairing makes every lane add the same two
 // values, so all lanes agree bit for bit) and then over the 4 wavefronts in a fixed order
 // through LDS, so the logits are identical run to run. Every lane of wavefront 0 then
