@@ -355,6 +355,26 @@ def test_zero_tokens_leaves_out_untouched():
     assert bool((out == 3.0).all())
 
 
+@pytest.mark.parametrize("bad", [dict(k=9), dict(d=200), dict(x_offset=2), dict(ws_short=True)])
+def test_rejected_call_enqueues_nothing(bad):
+    # an argument error returns before any launch: out keeps its contents
+    inp, d = small_case("reject", T=16, d=256, f=512)
+    out = torch.full((16, 256), 3.0, device="cuda")
+    x = d["x"]
+    if "x_offset" in bad:
+        x = x.data_ptr() + bad["x_offset"]  # misaligned
+    ws, ws_bytes = None, 0
+    if "ws_short" in bad:
+        ws = torch.empty(1024, dtype=torch.uint8, device="cuda")
+        ws_bytes = 1024
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_forward_ex(x, d["router_w"], d["w_gate"], d["w_up"], d["w_down"], d["scales"], None, out, 16,
+                           bad.get("d", 256), 512, 8, bad.get("k", 2), workspace=ws, workspace_bytes_=ws_bytes)
+    torch.cuda.synchronize()
+    assert ei.value.status in (moe.MOE_ERR_INVALID, moe.MOE_ERR_UNSUPPORTED)
+    assert bool((out == 3.0).all())
+
+
 # ------------------------------------------------------------------------------ invariants
 
 def test_run_to_run_bit_determinism():
