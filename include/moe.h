@@ -112,7 +112,9 @@ int moe_route(const void* x, const float* router_w, const float* router_bias,
    tokens to e; offsets = exclusive prefix sum [E+1]; perm[offsets[e] + r] = the r-th
    smallest token routed to e; pos[t][j] = index of (t, j) in perm. pos is -1 for padded
    tokens and for slots whose id is out of [0, E) or repeats an earlier slot of the same
-   token (such slots are not counted). Integer work; bit-exact. */
+   token (such slots are not counted). Integer work; bit-exact. From T = 4096 on the sort
+   runs over 1024-token chunks in parallel (same result), with its per-chunk counts in the
+   library workspace, which this call may then allocate. */
 int moe_dispatch(const int32_t* topk_ids, const uint8_t* pad_mask, int32_t* counts,
                  int32_t* offsets, int32_t* perm, int32_t* pos, int T, int E, int k, void* stream);
 

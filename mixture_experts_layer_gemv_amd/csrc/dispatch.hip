@@ -111,11 +111,123 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(const int32_t* __res
   }
 }
 
+// ------------------------------------------------------------------------------------
+// Large batches: the same counting sort over chunks of 1024 tokens in parallel. chunk
+// counts per expert (one workgroup per chunk), then one workgroup scans them into each
+// chunk's base position per expert, then each chunk ranks and scatters its tokens as pass 2
+// above does with a running base. A token's position is the same in both schemes, so the
+// arrays are identical.
+
+__global__ __launch_bounds__(kThreads) void dispatch_count_kernel(const int32_t* __restrict__ ids,
+                                                                  const uint8_t* __restrict__ pad_mask,
+                                                                  int32_t* __restrict__ chunk_counts, int T,
+                                                                  int E, int k) {
+  __shared__ int s_count[kMaxE];
+  const int tid = threadIdx.x;
+  if (tid < kMaxE) s_count[tid] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * kThreads + tid;
+  if (t < T && (pad_mask == nullptr || pad_mask[t] != 0)) {
+    const int32_t* it = ids + (size_t)t * k;
+    for (int j = 0; j < k; ++j)
+      if (slot_valid(it, j, E)) atomicAdd(&s_count[it[j]], 1);
+  }
+  __syncthreads();
+  if (tid < E) chunk_counts[(size_t)blockIdx.x * E + tid] = s_count[tid];
+}
+
+// counts, offsets, and chunk_base[c][e] = offsets[e] + sum over earlier chunks of their counts
+__global__ __launch_bounds__(kMaxE) void dispatch_scan_kernel(const int32_t* __restrict__ chunk_counts,
+                                                              int32_t* __restrict__ chunk_base,
+                                                              int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ offsets, int nchunks,
+                                                              int E) {
+  __shared__ int s_total[kMaxE];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E)
+    for (int c = 0; c < nchunks; ++c) total += chunk_counts[(size_t)c * E + e];
+  s_total[e] = total;
+  __syncthreads();
+  if (e < E) {
+    int base = 0;
+    for (int q = 0; q < e; ++q) base += s_total[q];
+    counts[e] = total;
+    offsets[e] = base;
+    if (e == E - 1) offsets[E] = base + total;
+    for (int c = 0; c < nchunks; ++c) {
+      chunk_base[(size_t)c * E + e] = base;
+      base += chunk_counts[(size_t)c * E + e];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(const int32_t* __restrict__ ids,
+                                                                    const uint8_t* __restrict__ pad_mask,
+                                                                    const int32_t* __restrict__ chunk_base,
+                                                                    int32_t* __restrict__ perm,
+                                                                    int32_t* __restrict__ pos, int T, int E,
+                                                                    int k) {
+  __shared__ int s_wave[kWaves][kMaxE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int t = blockIdx.x * kThreads + tid;
+  const bool real = t < T && (pad_mask == nullptr || pad_mask[t] != 0);
+  const int32_t* it = ids + (size_t)(t < T ? t : 0) * k;
+  uint64_t emask = 0;
+  if (real)
+    for (int j = 0; j < k; ++j)
+      if (slot_valid(it, j, E)) emask |= 1ull << it[j];
+  for (int e = 0; e < E; ++e) {
+    uint64_t m = __ballot((emask >> e) & 1ull);
+    if (lane == 0) s_wave[wave][e] = __popcll(m);
+  }
+  __syncthreads();
+  if (tid < E) {
+    int run = chunk_base[(size_t)blockIdx.x * E + tid];
+    for (int w = 0; w < kWaves; ++w) {
+      int c = s_wave[w][tid];
+      s_wave[w][tid] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  if (t < T)
+    for (int j = 0; j < k; ++j) pos[(size_t)t * k + j] = -1;
+  for (int e = 0; e < E; ++e) {
+    const bool has = (emask >> e) & 1ull;
+    uint64_t m = __ballot(has);
+    if (has) {
+      int p = s_wave[wave][e] + __popcll(m & lt_mask);
+      perm[p] = t;
+      for (int j = 0; j < k; ++j)
+        if (it[j] == e) {
+          pos[(size_t)t * k + j] = p;
+          break;  // later slots with the same id are repeats and stay -1
+        }
+    }
+  }
+}
+
+int dispatch_chunks(int T) { return T >= kDispatchChunkedMinT ? (T + kThreads - 1) / kThreads : 0; }
+
 hipError_t launch_dispatch(const int32_t* ids, const uint8_t* pad_mask, int32_t* counts,
                            int32_t* offsets, int32_t* perm, int32_t* pos, int T, int E, int k,
-                           hipStream_t stream) {
-  hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kThreads), 0, stream, ids, pad_mask, counts,
-                     offsets, perm, pos, T, E, k);
+                           int32_t* chunk_scratch, hipStream_t stream) {
+  const int nchunks = dispatch_chunks(T);
+  if (nchunks == 0 || chunk_scratch == nullptr) {
+    hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kThreads), 0, stream, ids, pad_mask, counts,
+                       offsets, perm, pos, T, E, k);
+    return hipGetLastError();
+  }
+  int32_t* chunk_counts = chunk_scratch;
+  int32_t* chunk_base = chunk_scratch + (size_t)nchunks * E;
+  hipLaunchKernelGGL(dispatch_count_kernel, dim3(nchunks), dim3(kThreads), 0, stream, ids, pad_mask, chunk_counts,
+                     T, E, k);
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kMaxE), 0, stream, chunk_counts, chunk_base, counts,
+                     offsets, nchunks, E);
+  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(nchunks), dim3(kThreads), 0, stream, ids, pad_mask, chunk_base,
+                     perm, pos, T, E, k);
   return hipGetLastError();
 }
 

@@ -19,9 +19,15 @@ hipError_t launch_prenorm_router(const uint16_t* h, const float* norm_pre, float
                                  int32_t* topk_ids, float* topk_w, int T, int d, int E, int k,
                                  hipStream_t stream);
 
+// T at or above which the dispatch runs over 1024-token chunks in parallel (three launches)
+constexpr int kDispatchChunkedMinT = 4096;
+// chunks of the parallel dispatch for T (0 below the threshold); its scratch holds
+// 2 * chunks * E int32
+int dispatch_chunks(int T);
+// chunk_scratch NULL: the single-workgroup dispatch at any T
 hipError_t launch_dispatch(const int32_t* ids, const uint8_t* pad_mask, int32_t* counts,
                            int32_t* offsets, int32_t* perm, int32_t* pos, int T, int E, int k,
-                           hipStream_t stream);
+                           int32_t* chunk_scratch, hipStream_t stream);
 
 // parts > 1: the contraction over d is split in `parts`; P (fp32, 2 * parts * T * k * f
 // elements) holds the partial sums, completed into H by a second launch.

@@ -66,7 +66,7 @@ int hip_fail(hipError_t e, const char* where) {
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
-  size_t ids, w, counts, offsets, perm, pos, h, y, gp, total;
+  size_t ids, w, counts, offsets, perm, pos, h, y, gp, dchunk, total;
   int splits, gparts;
 };
 
@@ -90,6 +90,8 @@ Layout make_layout(int T, int d, int f, int E, int k) {
   L.y = take((size_t)L.splits * tk * d * 4);
   L.gparts = gate_up_parts(T, d, f, E);
   L.gp = L.gparts > 1 ? take((size_t)2 * L.gparts * tk * f * 4) : 0;
+  const int nchunks = moe::dispatch_chunks(T);
+  L.dchunk = nchunks > 0 ? take((size_t)2 * nchunks * E * 4) : 0;
   L.total = at;
   return L;
 }
@@ -264,7 +266,8 @@ int moe_forward_ex(const void* x, const float* router_w, const int8_t* w_gate, c
   const auto* sc = static_cast<const uint16_t*>(scales);
 
   MOE_HIP(moe::launch_router(xb, router_w, router_bias, pad_mask, ids, w, T, d, E, k, s), "router");
-  MOE_HIP(moe::launch_dispatch(ids, pad_mask, counts, offsets, perm, pos, T, E, k, s), "dispatch");
+  auto* dch = L.dchunk ? reinterpret_cast<int32_t*>(ws + L.dchunk) : nullptr;
+  MOE_HIP(moe::launch_dispatch(ids, pad_mask, counts, offsets, perm, pos, T, E, k, dch, s), "dispatch");
   MOE_TRY(run_experts(xb, perm, offsets, w_gate, w_up, w_down, sc, h, y, L.splits, gp, L.gparts, T, d, f, E, k, s));
   MOE_HIP(moe::launch_combine(y, L.splits, (size_t)T * k * d, pos, w, pad_mask, out, T, d, k, s), "combine");
 
@@ -324,7 +327,8 @@ int moe_forward_dense(const void* x, const float* router_w, const int8_t* w_gate
   const auto* sc = static_cast<const uint16_t*>(scales);
   MOE_HIP(moe::launch_router(xb, router_w, router_bias, pad_mask, ids, w, T, d, E, k, s), "router");
   MOE_HIP(moe::launch_onehot_expand(ids, w, pad_mask, ids_all, gates, T, E, k, s), "onehot_expand");
-  MOE_HIP(moe::launch_dispatch(ids_all, pad_mask, counts, offsets, perm, pos, T, E, E, s), "dispatch");
+  auto* dch = L.dchunk ? reinterpret_cast<int32_t*>(in + L.dchunk) : nullptr;
+  MOE_HIP(moe::launch_dispatch(ids_all, pad_mask, counts, offsets, perm, pos, T, E, E, dch, s), "dispatch");
   MOE_TRY(run_experts(xb, perm, offsets, w_gate, w_up, w_down, sc, h, y, L.splits, gp, L.gparts, T, d, f, E, E, s));
   MOE_HIP(moe::launch_combine(y, L.splits, (size_t)T * E * d, pos, gates, pad_mask, out, T, d, E, s), "combine");
   return MOE_OK;
@@ -373,7 +377,8 @@ int moe_block_forward(const void* h, const float* norm_pre, const float* norm_po
   const auto* sc = static_cast<const uint16_t*>(scales);
   MOE_HIP(moe::launch_prenorm_router(hb, norm_pre, eps, xn, router_w, router_bias, pad_mask, ids, w, T, d, E, k, s),
           "prenorm_router");
-  MOE_HIP(moe::launch_dispatch(ids, pad_mask, counts, offsets, perm, pos, T, E, k, s), "dispatch");
+  auto* dch = L.dchunk ? reinterpret_cast<int32_t*>(in + L.dchunk) : nullptr;
+  MOE_HIP(moe::launch_dispatch(ids, pad_mask, counts, offsets, perm, pos, T, E, k, dch, s), "dispatch");
   MOE_TRY(run_experts(xn, perm, offsets, w_gate, w_up, w_down, sc, hh, y, L.splits, gp, L.gparts, T, d, f, E, k, s));
   MOE_HIP(moe::launch_combine_postnorm(y, L.splits, (size_t)T * k * d, pos, w, pad_mask, hb, norm_post, eps, h_out,
                                        T, d, k, s),
@@ -412,8 +417,12 @@ int moe_dispatch(const int32_t* topk_ids, const uint8_t* pad_mask, int32_t* coun
   MOE_TRY(check_ptr(offsets, "offsets", 4));
   MOE_TRY(check_ptr(pos, "pos", 4));
   if (T > 0) MOE_TRY(check_ptr(perm, "perm", 4));
+  // large batches: the chunked dispatch, its per-chunk counts in the library workspace
+  char* dch = nullptr;
+  const int nchunks = moe::dispatch_chunks(T);
+  if (nchunks > 0) MOE_TRY(library_workspace((size_t)2 * nchunks * E * 4, &dch));
   MOE_HIP(moe::launch_dispatch(topk_ids, pad_mask, counts, offsets, perm, pos, T, E, k,
-                               static_cast<hipStream_t>(stream)),
+                               reinterpret_cast<int32_t*>(dch), static_cast<hipStream_t>(stream)),
           "dispatch");
   return MOE_OK;
 }

@@ -183,7 +183,9 @@ def test_dispatch_parity_on_oracle_routing(name):
 
 
 @pytest.mark.parametrize("T,E,k,n_pad", [(1, 8, 2, 0), (1023, 8, 2, 100), (1025, 8, 2, 0), (3000, 5, 3, 17),
-                                         (200, 64, 4, 20), (50, 1, 1, 0), (40, 8, 2, 40), (8192, 8, 2, 0)])
+                                         (200, 64, 4, 20), (50, 1, 1, 0), (40, 8, 2, 40), (8192, 8, 2, 0),
+                                         # chunked (T >= 4096): ragged last chunk, E = 64, k = 1, all pads
+                                         (4096, 8, 2, 0), (5000, 64, 4, 333), (9000, 3, 1, 10), (4100, 8, 2, 4100)])
 def test_dispatch_edge_cases(T, E, k, n_pad):
     rng = np.random.default_rng(T + 7 * E + k)
     ids = np.array([rng.permutation(E)[:k] for _ in range(T)], dtype=np.int32).reshape(T, k)
