@@ -12,8 +12,8 @@
 //           running base per expert carried across chunks give the global rank. So the
 //           tokens of each expert appear in ascending t, which is the stable order.
 // A slot counts only if its id is in [0, E) and differs from the token's earlier slots.
-#include "device_common.h"
 #include "kernels.h"
+#include "router_common.h"
 
 namespace moe {
 
@@ -31,13 +31,39 @@ __device__ __forceinline__ bool slot_valid(const int32_t* ids_t, int j, int E) {
   return true;
 }
 
-__global__ __launch_bounds__(kThreads) void dispatch_kernel(const int32_t* __restrict__ ids,
-                                                            const uint8_t* __restrict__ pad_mask,
-                                                            int32_t* __restrict__ counts,
-                                                            int32_t* __restrict__ offsets,
-                                                            int32_t* __restrict__ perm,
-                                                            int32_t* __restrict__ pos, int T, int E,
-                                                            int k) {
+// Batches of at most 64 tokens: the same stable counting sort in one wavefront, lane t = token
+// t, without LDS or barriers. emask: the experts of the lane's valid slots; slot_of(e): the
+// first slot holding expert e. For each expert in order, a ballot gives its count and each
+// token's rank among the earlier tokens; the running sum of the counts is the offset. Lanes
+// >= T pass emask 0.
+template <typename SlotOf>
+__device__ __forceinline__ void dispatch_wave(uint64_t emask, SlotOf slot_of, int T, int E, int k,
+                                              int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                              int32_t* __restrict__ perm, int32_t* __restrict__ pos) {
+  const int t = threadIdx.x & 63;
+  const uint64_t lt_mask = (t == 0) ? 0ull : (~0ull >> (64 - t));
+  if (t < T)
+    for (int j = 0; j < k; ++j) pos[(size_t)t * k + j] = -1;
+  int base = 0;
+  for (int e = 0; e < E; ++e) {
+    const bool has = (emask >> e) & 1ull;
+    const uint64_t m = __ballot(has);
+    if (has) {
+      const int p = base + __popcll(m & lt_mask);
+      perm[p] = t;
+      pos[(size_t)t * k + slot_of(e)] = p;
+    }
+    if (t == 0) counts[e] = __popcll(m), offsets[e] = base;
+    base += __popcll(m);
+  }
+  if (t == 0) offsets[E] = base;
+}
+
+// The single-workgroup dispatch; every thread of the 1024 must call it.
+__device__ __forceinline__ void dispatch_block(const int32_t* __restrict__ ids, const uint8_t* __restrict__ pad_mask,
+                                               int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                               int32_t* __restrict__ perm, int32_t* __restrict__ pos, int T,
+                                               int E, int k) {
   __shared__ int s_count[kMaxE];
   __shared__ int s_base[kMaxE];
   __shared__ int s_wave[kWaves][kMaxE];
@@ -109,6 +135,91 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(const int32_t* __res
     if (tid < E) s_base[tid] += s_chunk[tid];
     __syncthreads();
   }
+}
+
+__global__ __launch_bounds__(kThreads) void dispatch_kernel(const int32_t* __restrict__ ids,
+                                                            const uint8_t* __restrict__ pad_mask,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ perm,
+                                                            int32_t* __restrict__ pos, int T, int E,
+                                                            int k) {
+  if (T <= 64) {
+    if (threadIdx.x >= 64) return;
+    const int t = threadIdx.x;
+    const int32_t* it = ids + (size_t)max(min(t, T - 1), 0) * k;
+    uint64_t emask = 0;
+    if (t < T && (pad_mask == nullptr || pad_mask[t] != 0))
+      for (int j = 0; j < k; ++j)
+        if (slot_valid(it, j, E)) emask |= 1ull << it[j];
+    auto slot_of = [&](int e) {
+      int j = 0;
+      while (it[j] != e) ++j;  // e is in emask, so some slot holds it
+      return j;
+    };
+    dispatch_wave(emask, slot_of, T, E, k, counts, offsets, perm, pos);
+    return;
+  }
+  dispatch_block(ids, pad_mask, counts, offsets, perm, pos, T, E, k);
+}
+
+// ------------------------------------------------------------------------------------
+// Routing of small batches, second half (the first is router_partial_kernel): thread
+// (t, e) = (tid / 8, tid % 8) adds token t's group sums for expert e in group order, lane
+// t < T of wavefront 0 takes the softmax and the top k (router_common.h); with kDispatch the
+// same wavefront then dispatches the experts it holds. E == 8, T <= kRouterSplitMaxT (64).
+template <bool kDispatch>
+__global__ __launch_bounds__(kThreads) void route_finish_kernel(
+    const float* __restrict__ partial, const float* __restrict__ router_bias, const uint8_t* __restrict__ pad_mask,
+    int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ pos, int T, int G, int k) {
+  constexpr int E = 8;
+  __shared__ float s_logit[kRouterSplitMaxT * E];
+  const int tid = threadIdx.x;
+  if (tid < T * E) {
+    const float* src = partial + (size_t)(tid / E) * G * E + (tid % E);
+    float logit = 0.0f;
+    constexpr int kBatch = 64;  // up to 64 loads in flight, then the adds in group order
+    for (int g0 = 0; g0 < G; g0 += kBatch) {
+      float v[kBatch];
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q)
+        if (g0 + q < G) v[q] = src[(size_t)(g0 + q) * E];
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q)
+        if (g0 + q < G) logit += v[q];
+    }
+    s_logit[tid] = logit;
+  }
+  __syncthreads();
+  if (tid >= 64) return;  // wavefront 0: lane t finishes token t (T <= 64)
+  uint64_t emask = 0;
+  uint32_t slots = 0;
+  if (tid < T) {
+    float p[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) p[e] = s_logit[tid * E + e];
+    const bool real = pad_mask == nullptr || pad_mask[tid] != 0;
+    emask = finish_token<E>(p, E, k, router_bias, real, topk_ids + (size_t)tid * k, topk_w + (size_t)tid * k,
+                            &slots);
+  }
+  if constexpr (kDispatch)
+    dispatch_wave(emask, [&](int e) { return (int)((slots >> (4 * e)) & 15u); }, T, E, k, counts, offsets, perm,
+                  pos);
+}
+
+hipError_t launch_route_finish(const float* partial, const float* router_bias, const uint8_t* pad_mask,
+                               int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                               int32_t* pos, int T, int d, int E, int k, hipStream_t stream) {
+  if (E != 8 || T <= 0 || T > kRouterSplitMaxT) return hipErrorInvalidValue;
+  const int G = d / 128;
+  if (counts != nullptr)
+    hipLaunchKernelGGL(route_finish_kernel<true>, dim3(1), dim3(kThreads), 0, stream, partial, router_bias,
+                       pad_mask, topk_ids, topk_w, counts, offsets, perm, pos, T, G, k);
+  else
+    hipLaunchKernelGGL(route_finish_kernel<false>, dim3(1), dim3(kThreads), 0, stream, partial, router_bias,
+                       pad_mask, topk_ids, topk_w, counts, offsets, perm, pos, T, G, k);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------------------

@@ -10,9 +10,27 @@ namespace moe {
 // T at or below which the expert FFN takes the weight-streaming (decode) kernels.
 constexpr int kDecodeMaxT = 64;
 
+// T at or below which routing with E == 8 can run in two launches: router_partial_kernel
+// (group sums, fp32 [T][d / 128][8]) and route_finish_kernel (sums, softmax, top-k, and
+// optionally the dispatch).
+constexpr int kRouterSplitMaxT = kDecodeMaxT;
+// floats of the group-sum scratch for (T, d, E); 0 where the two-launch routing does not apply
+size_t router_partial_floats(int T, int d, int E);
+hipError_t launch_router_partial(const uint16_t* x, const float* router_w, float* partial, int T, int d,
+                                 hipStream_t stream);
+// counts == NULL: routing only; otherwise the dispatch follows in the same launch
+// (counts, offsets, perm and pos as for launch_dispatch).
+hipError_t launch_route_finish(const float* partial, const float* router_bias, const uint8_t* pad_mask,
+                               int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                               int32_t* pos, int T, int d, int E, int k, hipStream_t stream);
+// partial NULL (or a batch the two-launch routing does not take): one launch
 hipError_t launch_router(const uint16_t* x, const float* router_w, const float* router_bias,
-                         const uint8_t* pad_mask, int32_t* topk_ids, float* topk_w, int T, int d,
-                         int E, int k, hipStream_t stream);
+                         const uint8_t* pad_mask, int32_t* topk_ids, float* topk_w, float* partial, int T,
+                         int d, int E, int k, hipStream_t stream);
+
+// x_norm = bf16(h * rnorm * norm_pre), bit-identical to what launch_prenorm_router writes
+hipError_t launch_rmsnorm(const uint16_t* h, const float* norm_pre, float eps, uint16_t* x_norm, int T, int d,
+                          hipStream_t stream);
 
 hipError_t launch_prenorm_router(const uint16_t* h, const float* norm_pre, float eps, uint16_t* x_norm,
                                  const float* router_w, const float* router_bias, const uint8_t* pad_mask,
@@ -55,9 +73,14 @@ hipError_t launch_combine(const float* Y, int splits, size_t part_stride, const 
                           const float* topk_w, const uint8_t* pad_mask, float* out, int T, int d,
                           int k, hipStream_t stream);
 
+// T at or above which the post-norm combine runs one workgroup per token (one launch);
+// below it, two launches over (T, d / 1024) workgroups with sumsq (fp32, T * ceil(d / 1024)
+// elements) as scratch. sumsq NULL: one workgroup per token at any T.
+constexpr int kCombineRowMinT = 1024;
+int combine_postnorm_scratch_floats(int T, int d);
 hipError_t launch_combine_postnorm(const float* Y, int splits, size_t part_stride, const int32_t* pos,
                                    const float* topk_w, const uint8_t* pad_mask, const uint16_t* h,
-                                   const float* norm_post, float eps, float* out, int T, int d, int k,
-                                   hipStream_t stream);
+                                   const float* norm_post, float eps, float* out, float* sumsq, int T, int d,
+                                   int k, hipStream_t stream);
 
 }  // namespace moe

@@ -66,7 +66,7 @@ int hip_fail(hipError_t e, const char* where) {
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
-  size_t ids, w, counts, offsets, perm, pos, h, y, gp, dchunk, total;
+  size_t ids, w, counts, offsets, perm, pos, h, y, gp, dchunk, rp, total;
   int splits, gparts;
 };
 
@@ -92,6 +92,8 @@ Layout make_layout(int T, int d, int f, int E, int k) {
   L.gp = L.gparts > 1 ? take((size_t)2 * L.gparts * tk * f * 4) : 0;
   const int nchunks = moe::dispatch_chunks(T);
   L.dchunk = nchunks > 0 ? take((size_t)2 * nchunks * E * 4) : 0;
+  const size_t rp_floats = moe::router_partial_floats(T, d, E);
+  L.rp = rp_floats > 0 ? take(rp_floats * 4) : 0;
   L.total = at;
   return L;
 }
@@ -116,6 +118,13 @@ DenseLayout make_dense_layout(int T, int d, int f, int E, int k) {
   D.total = at + D.L.total;
   return D;
 }
+
+// The MoE block's workspace starts with x_norm (bf16 [T][d]) and the post-norm combine's
+// chunk sums, followed by the layer's layout.
+size_t block_sumsq_bytes(int T, int d) {
+  return round_up((size_t)moe::combine_postnorm_scratch_floats(T, d) * 4, 256);
+}
+size_t block_prefix_bytes(int T, int d) { return round_up((size_t)T * d * 2, 256) + block_sumsq_bytes(T, d); }
 
 struct DeviceWorkspace {
   void* ptr = nullptr;
@@ -265,9 +274,17 @@ int moe_forward_ex(const void* x, const float* router_w, const int8_t* w_gate, c
   const auto* xb = static_cast<const uint16_t*>(x);
   const auto* sc = static_cast<const uint16_t*>(scales);
 
-  MOE_HIP(moe::launch_router(xb, router_w, router_bias, pad_mask, ids, w, T, d, E, k, s), "router");
-  auto* dch = L.dchunk ? reinterpret_cast<int32_t*>(ws + L.dchunk) : nullptr;
-  MOE_HIP(moe::launch_dispatch(ids, pad_mask, counts, offsets, perm, pos, T, E, k, dch, s), "dispatch");
+  if (L.rp) {
+    // small batches: group sums in parallel, then one launch adds them and dispatches
+    auto* rp = reinterpret_cast<float*>(ws + L.rp);
+    MOE_HIP(moe::launch_router_partial(xb, router_w, rp, T, d, s), "router");
+    MOE_HIP(moe::launch_route_finish(rp, router_bias, pad_mask, ids, w, counts, offsets, perm, pos, T, d, E, k, s),
+            "route+dispatch");
+  } else {
+    MOE_HIP(moe::launch_router(xb, router_w, router_bias, pad_mask, ids, w, nullptr, T, d, E, k, s), "router");
+    auto* dch = L.dchunk ? reinterpret_cast<int32_t*>(ws + L.dchunk) : nullptr;
+    MOE_HIP(moe::launch_dispatch(ids, pad_mask, counts, offsets, perm, pos, T, E, k, dch, s), "dispatch");
+  }
   MOE_TRY(run_experts(xb, perm, offsets, w_gate, w_up, w_down, sc, h, y, L.splits, gp, L.gparts, T, d, f, E, k, s));
   MOE_HIP(moe::launch_combine(y, L.splits, (size_t)T * k * d, pos, w, pad_mask, out, T, d, k, s), "combine");
 
@@ -325,7 +342,8 @@ int moe_forward_dense(const void* x, const float* router_w, const int8_t* w_gate
   auto* gp = reinterpret_cast<float*>(in + L.gp);
   const auto* xb = static_cast<const uint16_t*>(x);
   const auto* sc = static_cast<const uint16_t*>(scales);
-  MOE_HIP(moe::launch_router(xb, router_w, router_bias, pad_mask, ids, w, T, d, E, k, s), "router");
+  auto* rp = L.rp ? reinterpret_cast<float*>(in + L.rp) : nullptr;
+  MOE_HIP(moe::launch_router(xb, router_w, router_bias, pad_mask, ids, w, rp, T, d, E, k, s), "router");
   MOE_HIP(moe::launch_onehot_expand(ids, w, pad_mask, ids_all, gates, T, E, k, s), "onehot_expand");
   auto* dch = L.dchunk ? reinterpret_cast<int32_t*>(in + L.dchunk) : nullptr;
   MOE_HIP(moe::launch_dispatch(ids_all, pad_mask, counts, offsets, perm, pos, T, E, E, dch, s), "dispatch");
@@ -336,7 +354,7 @@ int moe_forward_dense(const void* x, const float* router_w, const int8_t* w_gate
 
 size_t moe_workspace_bytes_block(int T, int d, int f, int E, int k) {
   if (check_shape(T, d, f, E, k) != MOE_OK || T == 0) return 0;
-  return round_up((size_t)T * d * 2, 256) + make_layout(T, d, f, E, k).total;
+  return block_prefix_bytes(T, d) + make_layout(T, d, f, E, k).total;
 }
 
 int moe_block_forward(const void* h, const float* norm_pre, const float* norm_post, float eps,
@@ -351,8 +369,9 @@ int moe_block_forward(const void* h, const float* norm_pre, const float* norm_po
   if (router_bias && !aligned(router_bias, 4)) return fail(MOE_ERR_INVALID, "router_bias is not 4-byte aligned");
   if (T == 0) return MOE_OK;
   const size_t xbytes = round_up((size_t)T * d * 2, 256);
+  const size_t prefix = block_prefix_bytes(T, d);
   const Layout L = make_layout(T, d, f, E, k);
-  const size_t need = xbytes + L.total;
+  const size_t need = prefix + L.total;
   char* ws = nullptr;
   if (workspace) {
     if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID, "workspace is not 256-byte aligned");
@@ -363,7 +382,8 @@ int moe_block_forward(const void* h, const float* norm_pre, const float* norm_po
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   auto* xn = reinterpret_cast<uint16_t*>(ws);
-  char* in = ws + xbytes;
+  auto* sumsq = block_sumsq_bytes(T, d) ? reinterpret_cast<float*>(ws + xbytes) : nullptr;
+  char* in = ws + prefix;
   auto* ids = reinterpret_cast<int32_t*>(in + L.ids);
   auto* w = reinterpret_cast<float*>(in + L.w);
   auto* counts = reinterpret_cast<int32_t*>(in + L.counts);
@@ -375,13 +395,23 @@ int moe_block_forward(const void* h, const float* norm_pre, const float* norm_po
   auto* gp = reinterpret_cast<float*>(in + L.gp);
   const auto* hb = static_cast<const uint16_t*>(h);
   const auto* sc = static_cast<const uint16_t*>(scales);
-  MOE_HIP(moe::launch_prenorm_router(hb, norm_pre, eps, xn, router_w, router_bias, pad_mask, ids, w, T, d, E, k, s),
-          "prenorm_router");
-  auto* dch = L.dchunk ? reinterpret_cast<int32_t*>(in + L.dchunk) : nullptr;
-  MOE_HIP(moe::launch_dispatch(ids, pad_mask, counts, offsets, perm, pos, T, E, k, dch, s), "dispatch");
+  if (L.rp) {
+    // small batches: the norm, then the group sums in parallel, then routing + dispatch
+    auto* rp = reinterpret_cast<float*>(in + L.rp);
+    MOE_HIP(moe::launch_rmsnorm(hb, norm_pre, eps, xn, T, d, s), "rmsnorm");
+    MOE_HIP(moe::launch_router_partial(xn, router_w, rp, T, d, s), "router");
+    MOE_HIP(moe::launch_route_finish(rp, router_bias, pad_mask, ids, w, counts, offsets, perm, pos, T, d, E, k, s),
+            "route+dispatch");
+  } else {
+    MOE_HIP(moe::launch_prenorm_router(hb, norm_pre, eps, xn, router_w, router_bias, pad_mask, ids, w, T, d, E, k,
+                                       s),
+            "prenorm_router");
+    auto* dch = L.dchunk ? reinterpret_cast<int32_t*>(in + L.dchunk) : nullptr;
+    MOE_HIP(moe::launch_dispatch(ids, pad_mask, counts, offsets, perm, pos, T, E, k, dch, s), "dispatch");
+  }
   MOE_TRY(run_experts(xn, perm, offsets, w_gate, w_up, w_down, sc, hh, y, L.splits, gp, L.gparts, T, d, f, E, k, s));
   MOE_HIP(moe::launch_combine_postnorm(y, L.splits, (size_t)T * k * d, pos, w, pad_mask, hb, norm_post, eps, h_out,
-                                       T, d, k, s),
+                                       sumsq, T, d, k, s),
           "combine_postnorm");
   if (x_norm_out)
     MOE_HIP(hipMemcpyAsync(x_norm_out, xn, (size_t)T * d * 2, hipMemcpyDeviceToDevice, s), "x_norm copy");
@@ -403,8 +433,12 @@ int moe_route(const void* x, const float* router_w, const float* router_bias, co
   MOE_TRY(check_ptr(topk_ids, "topk_ids", 4));
   MOE_TRY(check_ptr(topk_w, "topk_w", 4));
   if (T == 0) return MOE_OK;
+  // small batches with E = 8: the group sums in the library workspace
+  char* rp = nullptr;
+  const size_t rp_floats = moe::router_partial_floats(T, d, E);
+  if (rp_floats > 0) MOE_TRY(library_workspace(rp_floats * 4, &rp));
   MOE_HIP(moe::launch_router(static_cast<const uint16_t*>(x), router_w, router_bias, pad_mask, topk_ids,
-                             topk_w, T, d, E, k, static_cast<hipStream_t>(stream)),
+                             topk_w, reinterpret_cast<float*>(rp), T, d, E, k, static_cast<hipStream_t>(stream)),
           "router");
   return MOE_OK;
 }

@@ -115,26 +115,48 @@ def check_layer(inp: dict, d: dict, rows=None, label=""):
 
 # ------------------------------------------------------------------------------ routing
 
-def test_router_is_batch_invariant_bitwise():
-    # large batches route 8 tokens per workgroup, small ones one: the same token must get the
-    # same ids and weights bit for bit either way (ragged last group included)
-    s = synth.custom("router_batches", T=1027, d=512, f=256, n_pad=9, bias=(0.5, 0, 0, 0, 0, 0, 0, -0.5))
+@pytest.mark.parametrize("dd", [512, 6144])
+def test_router_is_batch_invariant_bitwise(dd):
+    # from 1024 tokens the router takes 8 tokens per workgroup, from 65 one, up to 64 it sums
+    # 128-feature groups in parallel workgroups: the same token must get the same ids and
+    # weights bit for bit whichever runs (ragged last groups included)
+    s = synth.custom("router_batches", T=1027, d=dd, f=256, n_pad=9, bias=(0.5, 0, 0, 0, 0, 0, 0, -0.5))
     inp = synth.make_inputs(s, with_weights=False)
     d = to_dev(inp, with_weights=False)
     ids = torch.empty((s.T, s.k), dtype=torch.int32, device="cuda")
     w = torch.empty((s.T, s.k), dtype=torch.float32, device="cuda")
     moe.moe_route(d["x"], d["router_w"], d["router_bias"], d["pad_mask"], ids, w, s.T, s.d, s.E, s.k)
-    ids_b = torch.empty_like(ids)
-    w_b = torch.empty_like(w)
-    for a in range(0, s.T, 300):
-        b = min(s.T, a + 300)
-        moe.moe_route(d["x"][a:b], d["router_w"], d["router_bias"], d["pad_mask"][a:b], ids_b[a:b], w_b[a:b],
-                      b - a, s.d, s.E, s.k)
-    torch.cuda.synchronize()
-    assert torch.equal(ids, ids_b) and torch.equal(w, w_b)
+    for chunk in (300, 64, 13, 1):
+        ids_b = torch.full_like(ids, -7)
+        w_b = torch.full_like(w, float("nan"))
+        for a in range(0, s.T, chunk):
+            b = min(s.T, a + chunk)
+            moe.moe_route(d["x"][a:b], d["router_w"], d["router_bias"], d["pad_mask"][a:b], ids_b[a:b], w_b[a:b],
+                          b - a, s.d, s.E, s.k)
+        torch.cuda.synchronize()
+        assert torch.equal(ids, ids_b) and torch.equal(w, w_b), chunk
     r = oracle.route(inp["x"], inp["router_w"], inp["router_bias"], inp["pad_mask"], s.k)
     excl, amb = exclusions(r)
     compare_ids(ids.cpu().numpy(), r["ids"], excl, amb)
+
+
+def test_forward_routing_matches_route_bitwise():
+    # moe_forward at T <= 64 finishes the routing inside the dispatch launch: its ids and
+    # weights are those of moe_route on the same rows, bit for bit
+    s = synth.custom("fwd_route", T=100, d=1024, f=256, n_pad=7, bias=(0.2, 0, 0, 0, 0, 0, -0.1, 0))
+    inp = synth.make_inputs(s)
+    d = to_dev(inp)
+    T = 40
+    small = dict(d, x=d["x"][:T], pad_mask=d["pad_mask"][:T])
+    _, dbg = run_forward(small, T, s.d, s.f, s.E, s.k)
+    ids = torch.empty((s.T, s.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((s.T, s.k), dtype=torch.float32, device="cuda")
+    # 100 tokens: one workgroup per token
+    moe.moe_route(d["x"], d["router_w"], d["router_bias"], d["pad_mask"], ids, w, s.T, s.d, s.E, s.k)
+    torch.cuda.synchronize()
+    assert np.array_equal(dbg["topk_ids"], ids.cpu().numpy()[:T])
+    assert np.array_equal(dbg["topk_w"].view(np.uint32), w.cpu().numpy()[:T].view(np.uint32))
+    assert (inp["pad_mask"][:T] == 0).any()
 
 
 @pytest.mark.parametrize("name", CONFIG_NAMES)
@@ -182,7 +204,9 @@ def test_dispatch_parity_on_oracle_routing(name):
     print(f"[{name}] dispatch counts {ref['counts'].tolist()}", flush=True)
 
 
-@pytest.mark.parametrize("T,E,k,n_pad", [(1, 8, 2, 0), (1023, 8, 2, 100), (1025, 8, 2, 0), (3000, 5, 3, 17),
+# up to 64 tokens one wavefront dispatches (ballots), above one workgroup, from 4096 chunks
+@pytest.mark.parametrize("T,E,k,n_pad", [(1, 8, 2, 0), (64, 64, 4, 5), (64, 8, 2, 0), (65, 8, 2, 3), (17, 3, 3, 2),
+                                         (1023, 8, 2, 100), (1025, 8, 2, 0), (3000, 5, 3, 17),
                                          (200, 64, 4, 20), (50, 1, 1, 0), (40, 8, 2, 40), (8192, 8, 2, 0),
                                          # chunked (T >= 4096): ragged last chunk, E = 64, k = 1, all pads
                                          (4096, 8, 2, 0), (5000, 64, 4, 333), (9000, 3, 1, 10), (4100, 8, 2, 4100)])

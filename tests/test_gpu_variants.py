@@ -149,8 +149,33 @@ def block_case(s, inp, d, rows):
         assert np.array_equal(got[padded], synth.bf16_bits_to_f32(inp["x"][padded]))
 
 
-@pytest.mark.parametrize("case", ["tiny", "decode", "batched_decode", dict(T=500, d=256, f=512, n_pad=40)])
+# below 1024 tokens the post-norm combine takes two launches over (token, 1024-column chunk)
+# workgroups, from 1024 one workgroup per token (and the router 8 tokens per workgroup);
+# d = 1280 leaves a partial last chunk
+@pytest.mark.parametrize("case", ["tiny", "decode", "batched_decode", dict(T=500, d=256, f=512, n_pad=40),
+                                  dict(T=40, d=1280, f=256, n_pad=5), dict(T=1100, d=1280, f=256, n_pad=60)])
 def test_block_parity(case):
     s, inp, d = grok_case(case) if isinstance(case, str) else small("block", **case)
     rows = np.arange(s.T) if s.T * s.d <= 200_000 else sample_rows(s.T, 12, seed=4)
     block_case(s, inp, d, rows)
+
+
+def test_block_prenorm_is_batch_invariant_bitwise():
+    """A token's normalised MoE input is the same bits whether its batch takes the separate norm
+    launch (up to 64 tokens), the one-token or the 8-token router workgroups."""
+    s, inp, d = small("block_inv", T=1040, d=1280, f=256)
+    wpre = torch.from_numpy((1 + 0.1 * np.random.default_rng(12).standard_normal(s.d)).astype(np.float32)).cuda()
+    wpost = torch.ones(s.d, dtype=torch.float32, device="cuda")
+
+    def x_norm(T):
+        h_out = torch.empty((T, s.d), device="cuda")
+        xn = torch.empty((T, s.d), dtype=torch.int16, device="cuda")
+        moe.moe_block_forward(d["x"][:T], wpre, wpost, 1e-5, d["router_w"], d["w_gate"], d["w_up"], d["w_down"],
+                              d["scales"], None, h_out, T, s.d, s.f, s.E, s.k, router_bias=d["router_bias"],
+                              x_norm_out=xn)
+        torch.cuda.synchronize()
+        return xn.cpu().numpy()
+
+    full = x_norm(s.T)
+    assert np.array_equal(full[:24], x_norm(24))
+    assert np.array_equal(full[:100], x_norm(100))
