@@ -12,7 +12,7 @@
 namespace moe {
 
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Y, int splits,
-                                                      size_t part_stride,
+                                                      const int* __restrict__ splits_dev, size_t part_stride,
                                                       const int32_t* __restrict__ pos,
                                                       const float* __restrict__ topk_w,
                                                       const uint8_t* __restrict__ pad_mask,
@@ -20,6 +20,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int t = blockIdx.x;
   const int c = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
   if (c >= d) return;
+  if (splits_dev) splits = *splits_dev;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (pad_mask == nullptr || pad_mask[t] != 0) {
     for (int j = 0; j < k; ++j) {
@@ -92,11 +93,13 @@ __device__ __forceinline__ f32x4 residual_postnorm(const f32x4& m, float r, cons
 // chunk sums (the LDS slot alternates between chunks, so one barrier per chunk suffices); the
 // second rescales in place (each thread rereads only its own writes) and adds h.
 __global__ __launch_bounds__(256) void combine_postnorm_kernel(
-    const float* __restrict__ Y, int splits, size_t part_stride, const int32_t* __restrict__ pos,
+    const float* __restrict__ Y, int splits, const int* __restrict__ splits_dev, size_t part_stride,
+    const int32_t* __restrict__ pos,
     const float* __restrict__ topk_w, const uint8_t* __restrict__ pad_mask, const uint16_t* __restrict__ h,
     const float* __restrict__ norm_post, float eps, float* __restrict__ out, int d, int k) {
   __shared__ float s_red[2][4];
   const int t = blockIdx.x, tid = threadIdx.x;
+  if (splits_dev) splits = *splits_dev;
   const bool real = pad_mask == nullptr || pad_mask[t] != 0;
   float* row = out + (size_t)t * d;
   const int nchunks = (d + 1023) / 1024;
@@ -120,13 +123,15 @@ __global__ __launch_bounds__(256) void combine_postnorm_kernel(
 // Small batches, first launch: grid (T, chunks); m of the chunk into h_out, its chunk sum
 // into sumsq[t][chunk].
 __global__ __launch_bounds__(256) void combine_sumsq_kernel(const float* __restrict__ Y, int splits,
-                                                            size_t part_stride, const int32_t* __restrict__ pos,
+                                                            const int* __restrict__ splits_dev, size_t part_stride,
+                                                            const int32_t* __restrict__ pos,
                                                             const float* __restrict__ topk_w,
                                                             const uint8_t* __restrict__ pad_mask,
                                                             float* __restrict__ out, float* __restrict__ sumsq,
                                                             int d, int k) {
   __shared__ float s_red[4];
   const int t = blockIdx.x, i = blockIdx.y;
+  if (splits_dev) splits = *splits_dev;
   const int c = i * 1024 + threadIdx.x * 4;
   f32x4 m = {0.f, 0.f, 0.f, 0.f};
   if (c < d) {
@@ -157,29 +162,30 @@ int combine_postnorm_scratch_floats(int T, int d) {
   return T < kCombineRowMinT ? T * ((d + 1023) / 1024) : 0;
 }
 
-hipError_t launch_combine_postnorm(const float* Y, int splits, size_t part_stride, const int32_t* pos,
+hipError_t launch_combine_postnorm(const float* Y, int splits, const int* splits_dev, size_t part_stride,
+                                   const int32_t* pos,
                                    const float* topk_w, const uint8_t* pad_mask, const uint16_t* h,
                                    const float* norm_post, float eps, float* out, float* sumsq, int T, int d,
                                    int k, hipStream_t stream) {
   if (T < kCombineRowMinT && sumsq != nullptr) {
     const dim3 grid(T, (d + 1023) / 1024);
-    hipLaunchKernelGGL(combine_sumsq_kernel, grid, dim3(256), 0, stream, Y, splits, part_stride, pos, topk_w,
-                       pad_mask, out, sumsq, d, k);
+    hipLaunchKernelGGL(combine_sumsq_kernel, grid, dim3(256), 0, stream, Y, splits, splits_dev, part_stride, pos,
+                       topk_w, pad_mask, out, sumsq, d, k);
     hipLaunchKernelGGL(postnorm_residual_kernel, grid, dim3(256), 0, stream, sumsq, h, norm_post, eps, out, d);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(combine_postnorm_kernel, dim3(T), dim3(256), 0, stream, Y, splits, part_stride, pos, topk_w,
-                     pad_mask, h, norm_post, eps, out, d, k);
+  hipLaunchKernelGGL(combine_postnorm_kernel, dim3(T), dim3(256), 0, stream, Y, splits, splits_dev, part_stride,
+                     pos, topk_w, pad_mask, h, norm_post, eps, out, d, k);
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const float* Y, int splits, size_t part_stride, const int32_t* pos,
-                          const float* topk_w, const uint8_t* pad_mask, float* out, int T, int d,
-                          int k, hipStream_t stream) {
+hipError_t launch_combine(const float* Y, int splits, const int* splits_dev, size_t part_stride,
+                          const int32_t* pos, const float* topk_w, const uint8_t* pad_mask, float* out,
+                          int T, int d, int k, hipStream_t stream) {
   // small batches: 256 columns per workgroup, so that more CUs share the gather
   const int threads = T <= kDecodeMaxT ? 64 : 256;
   dim3 grid(T, (d + 4 * threads - 1) / (4 * threads));
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(threads), 0, stream, Y, splits, part_stride, pos,
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(threads), 0, stream, Y, splits, splits_dev, part_stride, pos,
                      topk_w, pad_mask, out, d, k);
   return hipGetLastError();
 }

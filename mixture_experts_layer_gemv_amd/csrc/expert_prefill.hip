@@ -119,6 +119,7 @@ __device__ __forceinline__ void store_col(uint16_t* sB, int row, int koff, const
 // few activation and weight tiles in its L2.
 struct TileOrder {
   int nslots, ntiles, xm, xn, ngroup;
+  int ncu;  // compute units: one workgroup of this kernel fits a CU (144 KiB of LDS)
 };
 
 __device__ __forceinline__ void tile_of(int w, const TileOrder& o, int& mslot, int& ntile) {
@@ -132,15 +133,34 @@ __device__ __forceinline__ void tile_of(int w, const TileOrder& o, int& mslot, i
   ntile = xj * nblk + g * o.ngroup + rem % o.ngroup;
 }
 
+// Parts of the down contraction when the kernel may choose 1 or 2: the live workgroups run in
+// rounds of ncu (one per CU); two parts fill a ragged last round better but cost a second fp32
+// partial, 8 bytes per output element (written, then read by the combine) at about 5 TB/s
+// against 2 f FLOPs at about 1 PFLOP/s, i.e. about 800 / f of the kernel's time.
+__device__ __forceinline__ int down_parts(const int32_t* offsets, int E, int ntiles, int ncu, int f) {
+  int live = 0;
+  for (int e = 0; e < E; ++e) live += (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+  if (live == 0) return 1;
+  const float r1 = (float)(live * ntiles) / (float)ncu, r2 = 2.0f * r1;
+  const float fill1 = ceilf(r1) / r1, fill2 = ceilf(r2) / r2;
+  return fill1 > fill2 + 800.0f / (float)f ? 2 : 1;
+}
+
 template <bool kGateUp>
 __global__ __launch_bounds__(kThreads) void expert_prefill_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, const int8_t* __restrict__ B0,
     const int8_t* __restrict__ B1, const uint16_t* __restrict__ scales, void* __restrict__ out,
-    int d, int f, int E, int rows_cap, TileOrder order) {
+    int d, int f, int E, int rows_cap, TileOrder order, int* __restrict__ splits_used) {
   using Frag = typename PrefillTraits<kGateUp>::Frag;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE_ELEMS];
 
+  int parts = gridDim.z;
+  if (!kGateUp && splits_used != nullptr) {  // launched with 2 parts: keep 1 or 2
+    parts = down_parts(offsets, E, order.ntiles, order.ncu, f);
+    if (blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x == 0) *splits_used = parts;
+    if ((int)blockIdx.z >= parts) return;
+  }
   int mslot, ntile;
   tile_of(blockIdx.x, order, mslot, ntile);
   int e, row0, rows;
@@ -148,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void expert_prefill_kernel(
 
   const int K = kGateUp ? d : f;  // contraction length
   const int N = kGateUp ? f : d;  // columns of each weight matrix
-  const int kspan = K / gridDim.z, kbeg = blockIdx.z * kspan;
+  const int kspan = K / parts, kbeg = blockIdx.z * kspan;
   const int n0 = ntile * (kGateUp ? HALF : 2 * HALF);
   const uint32_t ldb = (uint32_t)N;
 
@@ -276,17 +296,31 @@ __global__ __launch_bounds__(kThreads) void expert_prefill_kernel(
   gload(R1, min(BK, klast));
   lds_store(R0, L0);
   __syncthreads();
-  for (int it = 0; it < nslices; it += 2) {
-    gload(R0, min((it + 2) * BK, klast));
-    slice(L0);
-    lds_store(R1, L1);
-    interleave();
-    __syncthreads();
-    gload(R1, min((it + 3) * BK, klast));
-    slice(L1);
-    lds_store(R0, L0);
-    interleave();
-    __syncthreads();
+  if (__builtin_amdgcn_readfirstlane(wm * 64 < rows ? 1 : 0)) {  // uniform per wavefront
+    for (int it = 0; it < nslices; it += 2) {
+      gload(R0, min((it + 2) * BK, klast));
+      slice(L0);
+      lds_store(R1, L1);
+      interleave();
+      __syncthreads();
+      gload(R1, min((it + 3) * BK, klast));
+      slice(L1);
+      lds_store(R0, L0);
+      interleave();
+      __syncthreads();
+    }
+  } else {
+    // every row of this wavefront's 64 is past the tile end (the last tile of a segment):
+    // it only moves the slices, with the same barriers, and leaves the MFMA pipe of its SIMD
+    // to the other wavefront there (waves w and w + 4 share a SIMD: wm 0 / 2 and 1 / 3)
+    for (int it = 0; it < nslices; it += 2) {
+      gload(R0, min((it + 2) * BK, klast));
+      lds_store(R1, L1);
+      __syncthreads();
+      gload(R1, min((it + 3) * BK, klast));
+      lds_store(R0, L0);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: lane holds, per tile (mt, nt), rows wm*64 + 32 mt + 8 (i/4) + 4 (lane/32)
@@ -340,7 +374,11 @@ int prefill_mslots(int rows_cap, int E) { return ((rows_cap + BM - 1) / BM + E +
 // xn = n-tile blocks across XCDs (the rest of the 8 split the m-slots), as preferred by
 // the caller when the tile counts allow it; ngroup = n-tiles swept together.
 TileOrder make_order(int nslots, int ntiles, int xn_pref) {
-  TileOrder o{nslots, ntiles, 8, 1, 1};
+  int dev = 0, ncu = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+    ncu = 256;
+  TileOrder o{nslots, ntiles, 8, 1, 1, ncu};
   for (int xn = xn_pref; xn >= 1; xn /= 2)
     if (ntiles % xn == 0) {
       o.xn = xn;
@@ -364,20 +402,21 @@ hipError_t launch_gate_up_prefill(const uint16_t* x, const int32_t* perm, const 
   const TileOrder order = make_order(nslots, ntiles, 8);
   dim3 grid(nslots * ntiles, 1, 1);
   hipLaunchKernelGGL(expert_prefill_kernel<true>, grid, dim3(kThreads), 0, stream, x, perm, offsets,
-                     w_gate, w_up, scales, (void*)H, d, f, E, rows_cap, order);
+                     w_gate, w_up, scales, (void*)H, d, f, E, rows_cap, order, (int*)nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_down_prefill(const _Float16* H, const int32_t* offsets, const int8_t* w_down,
                                const uint16_t* scales, float* Y, int splits, int rows_cap, int d,
-                               int f, int E, hipStream_t stream) {
+                               int f, int E, int* splits_used, hipStream_t stream) {
+  if (splits_used != nullptr && splits != 2) return hipErrorInvalidValue;
   const int nslots = prefill_mslots(rows_cap, E), ntiles = d / (2 * HALF);
   // H can exceed the last-level cache: split the XCDs 2 (rows) x 4 (columns)
   const TileOrder order = make_order(nslots, ntiles, 4);
   dim3 grid(nslots * ntiles, 1, splits);
   hipLaunchKernelGGL(expert_prefill_kernel<false>, grid, dim3(kThreads), 0, stream,
                      reinterpret_cast<const uint16_t*>(H), (const int32_t*)nullptr, offsets, w_down,
-                     (const int8_t*)nullptr, scales, (void*)Y, d, f, E, rows_cap, order);
+                     (const int8_t*)nullptr, scales, (void*)Y, d, f, E, rows_cap, order, splits_used);
   return hipGetLastError();
 }
 

@@ -62,23 +62,28 @@ hipError_t launch_gate_up_prefill(const uint16_t* x, const int32_t* perm, const 
                                   const int8_t* w_gate, const int8_t* w_up, const uint16_t* scales,
                                   _Float16* H, int rows_cap, int d, int f, int E, hipStream_t stream);
 
+// splits_used NULL: exactly `splits` parts. Otherwise (splits == 2) the kernel keeps one or
+// two parts, whichever fills the chip's rounds of workgroups better net of the second
+// partial's traffic, and writes the count to *splits_used for launch_combine.
 hipError_t launch_down_prefill(const _Float16* H, const int32_t* offsets, const int8_t* w_down,
                                const uint16_t* scales, float* Y, int splits, int rows_cap, int d,
-                               int f, int E, hipStream_t stream);
+                               int f, int E, int* splits_used, hipStream_t stream);
 
 hipError_t launch_onehot_expand(const int32_t* ids, const float* w, const uint8_t* pad_mask,
                                 int32_t* ids_all, float* gates, int T, int E, int k, hipStream_t stream);
 
-hipError_t launch_combine(const float* Y, int splits, size_t part_stride, const int32_t* pos,
-                          const float* topk_w, const uint8_t* pad_mask, float* out, int T, int d,
-                          int k, hipStream_t stream);
+// splits_dev non-NULL: the number of partials is read there (written by the down kernel)
+hipError_t launch_combine(const float* Y, int splits, const int* splits_dev, size_t part_stride,
+                          const int32_t* pos, const float* topk_w, const uint8_t* pad_mask, float* out,
+                          int T, int d, int k, hipStream_t stream);
 
 // T at or above which the post-norm combine runs one workgroup per token (one launch);
 // below it, two launches over (T, d / 1024) workgroups with sumsq (fp32, T * ceil(d / 1024)
 // elements) as scratch. sumsq NULL: one workgroup per token at any T.
 constexpr int kCombineRowMinT = 1024;
 int combine_postnorm_scratch_floats(int T, int d);
-hipError_t launch_combine_postnorm(const float* Y, int splits, size_t part_stride, const int32_t* pos,
+hipError_t launch_combine_postnorm(const float* Y, int splits, const int* splits_dev, size_t part_stride,
+                                   const int32_t* pos,
                                    const float* topk_w, const uint8_t* pad_mask, const uint16_t* h,
                                    const float* norm_post, float eps, float* out, float* sumsq, int T, int d,
                                    int k, hipStream_t stream);

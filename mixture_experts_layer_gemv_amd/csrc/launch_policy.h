@@ -1,20 +1,24 @@
-// Launch policy of the decode expert kernels (T <= 64): how many parts the contractions are
-// split into. The kernels stream each touched expert's weights once; a split only adds
+// Launch policy of the expert kernels: how many parts the contractions are split into. The
+// decode kernels (T <= 64) stream each touched expert's weights once; a split only adds
 // wavefronts (and fp32 partial sums) when the 256-column slabs alone would leave the chip
-// under-filled, e.g. at one GPU's share of a tensor-parallel split over f.
+// under-filled, e.g. at one GPU's share of a tensor-parallel split over f. The prefill down
+// kernel splits to fill a ragged last round of workgroups.
 #pragma once
 
 #include "kernels.h"
 
 namespace moe {
 
-// Targets measured on whole forward passes at the Grok-1 shape and at one GPU's
-// tensor-parallel share: the down projection wants about 1024 workgroups while each
-// wavefront carries one 16-row tile (T <= 16) and about 512 with two (longer streams win
+// Small batches (T <= 64), targets measured on whole forward passes at the Grok-1 shape and
+// at one GPU's tensor-parallel share: the down projection wants about 1024 workgroups while
+// each wavefront carries one 16-row tile (T <= 16) and about 512 with two (longer streams win
 // once the MFMA work per byte doubles), with parts of at least 1024 rows (shorter ones lose
 // to their start-up). At most 8 parts, each a whole number of 128-row steps.
+// Large batches: the most parts the prefill down kernel may use. Launched with 2, it keeps
+// 1 or 2 on the device (from the live tile count, which only the device knows) and reports
+// the choice to the combine.
 inline int down_splits(int T, int d, int f, int E) {
-  if (T > kDecodeMaxT) return 1;
+  if (T > kDecodeMaxT) return f >= 8192 ? 2 : 1;
   const long slabs = (long)(d / 256) * E;
   const long target = T <= 16 ? 1024 : 512;
   int s = 1;

@@ -66,7 +66,7 @@ int hip_fail(hipError_t e, const char* where) {
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
-  size_t ids, w, counts, offsets, perm, pos, h, y, gp, dchunk, rp, total;
+  size_t ids, w, counts, offsets, perm, pos, h, y, gp, dchunk, rp, sused, total;
   int splits, gparts;
 };
 
@@ -94,6 +94,8 @@ Layout make_layout(int T, int d, int f, int E, int k) {
   L.dchunk = nchunks > 0 ? take((size_t)2 * nchunks * E * 4) : 0;
   const size_t rp_floats = moe::router_partial_floats(T, d, E);
   L.rp = rp_floats > 0 ? take(rp_floats * 4) : 0;
+  // large batches: the number of down parts the prefill kernel kept (it may keep 1 of 2)
+  L.sused = (T > moe::kDecodeMaxT && L.splits == 2) ? take(4) : 0;
   L.total = at;
   return L;
 }
@@ -177,9 +179,11 @@ int check_layer_args(const void* x, const float* router_w, const int8_t* w_gate,
   return MOE_OK;
 }
 
+// splits_used: where the prefill down kernel reports the parts it kept (NULL: exactly `splits`)
 int run_experts(const uint16_t* x, const int32_t* perm, const int32_t* offsets, const int8_t* w_gate,
                 const int8_t* w_up, const int8_t* w_down, const uint16_t* scales, _Float16* h,
-                float* y, int splits, float* gp, int gparts, int T, int d, int f, int E, int k, hipStream_t s) {
+                float* y, int splits, int* splits_used, float* gp, int gparts, int T, int d, int f, int E, int k,
+                hipStream_t s) {
   const int rows_cap = T * k;
   if (T <= moe::kDecodeMaxT) {
     MOE_HIP(moe::launch_gate_up_decode(x, perm, offsets, w_gate, w_up, scales, h, gp, gparts, T, k, d, f, E, s),
@@ -188,7 +192,8 @@ int run_experts(const uint16_t* x, const int32_t* perm, const int32_t* offsets, 
   } else {
     MOE_HIP(moe::launch_gate_up_prefill(x, perm, offsets, w_gate, w_up, scales, h, rows_cap, d, f, E, s),
             "gate_up");
-    MOE_HIP(moe::launch_down_prefill(h, offsets, w_down, scales, y, splits, rows_cap, d, f, E, s), "down");
+    MOE_HIP(moe::launch_down_prefill(h, offsets, w_down, scales, y, splits, rows_cap, d, f, E, splits_used, s),
+            "down");
   }
   return MOE_OK;
 }
@@ -285,8 +290,10 @@ int moe_forward_ex(const void* x, const float* router_w, const int8_t* w_gate, c
     auto* dch = L.dchunk ? reinterpret_cast<int32_t*>(ws + L.dchunk) : nullptr;
     MOE_HIP(moe::launch_dispatch(ids, pad_mask, counts, offsets, perm, pos, T, E, k, dch, s), "dispatch");
   }
-  MOE_TRY(run_experts(xb, perm, offsets, w_gate, w_up, w_down, sc, h, y, L.splits, gp, L.gparts, T, d, f, E, k, s));
-  MOE_HIP(moe::launch_combine(y, L.splits, (size_t)T * k * d, pos, w, pad_mask, out, T, d, k, s), "combine");
+  auto* su = L.sused ? reinterpret_cast<int*>(ws + L.sused) : nullptr;
+  MOE_TRY(run_experts(xb, perm, offsets, w_gate, w_up, w_down, sc, h, y, L.splits, su, gp, L.gparts, T, d, f, E, k,
+                      s));
+  MOE_HIP(moe::launch_combine(y, L.splits, su, (size_t)T * k * d, pos, w, pad_mask, out, T, d, k, s), "combine");
 
   if (dbg) {
     const size_t tk = (size_t)T * k;
@@ -347,8 +354,10 @@ int moe_forward_dense(const void* x, const float* router_w, const int8_t* w_gate
   MOE_HIP(moe::launch_onehot_expand(ids, w, pad_mask, ids_all, gates, T, E, k, s), "onehot_expand");
   auto* dch = L.dchunk ? reinterpret_cast<int32_t*>(in + L.dchunk) : nullptr;
   MOE_HIP(moe::launch_dispatch(ids_all, pad_mask, counts, offsets, perm, pos, T, E, E, dch, s), "dispatch");
-  MOE_TRY(run_experts(xb, perm, offsets, w_gate, w_up, w_down, sc, h, y, L.splits, gp, L.gparts, T, d, f, E, E, s));
-  MOE_HIP(moe::launch_combine(y, L.splits, (size_t)T * E * d, pos, gates, pad_mask, out, T, d, E, s), "combine");
+  auto* su = L.sused ? reinterpret_cast<int*>(in + L.sused) : nullptr;
+  MOE_TRY(run_experts(xb, perm, offsets, w_gate, w_up, w_down, sc, h, y, L.splits, su, gp, L.gparts, T, d, f, E, E,
+                      s));
+  MOE_HIP(moe::launch_combine(y, L.splits, su, (size_t)T * E * d, pos, gates, pad_mask, out, T, d, E, s), "combine");
   return MOE_OK;
 }
 
@@ -409,8 +418,10 @@ int moe_block_forward(const void* h, const float* norm_pre, const float* norm_po
     auto* dch = L.dchunk ? reinterpret_cast<int32_t*>(in + L.dchunk) : nullptr;
     MOE_HIP(moe::launch_dispatch(ids, pad_mask, counts, offsets, perm, pos, T, E, k, dch, s), "dispatch");
   }
-  MOE_TRY(run_experts(xn, perm, offsets, w_gate, w_up, w_down, sc, hh, y, L.splits, gp, L.gparts, T, d, f, E, k, s));
-  MOE_HIP(moe::launch_combine_postnorm(y, L.splits, (size_t)T * k * d, pos, w, pad_mask, hb, norm_post, eps, h_out,
+  auto* su = L.sused ? reinterpret_cast<int*>(in + L.sused) : nullptr;
+  MOE_TRY(run_experts(xn, perm, offsets, w_gate, w_up, w_down, sc, hh, y, L.splits, su, gp, L.gparts, T, d, f, E, k,
+                      s));
+  MOE_HIP(moe::launch_combine_postnorm(y, L.splits, su, (size_t)T * k * d, pos, w, pad_mask, hb, norm_post, eps, h_out,
                                        sumsq, T, d, k, s),
           "combine_postnorm");
   if (x_norm_out)
@@ -507,7 +518,7 @@ int moe_down(const void* h, const int32_t* offsets, const int8_t* w_down, const 
   if (T <= moe::kDecodeMaxT)
     MOE_HIP(moe::launch_down_decode(hh, offsets, w_down, sc, y, splits, T * k, T, d, f, E, s), "down");
   else
-    MOE_HIP(moe::launch_down_prefill(hh, offsets, w_down, sc, y, splits, T * k, d, f, E, s), "down");
+    MOE_HIP(moe::launch_down_prefill(hh, offsets, w_down, sc, y, splits, T * k, d, f, E, nullptr, s), "down");
   return MOE_OK;
 }
 
@@ -520,7 +531,7 @@ int moe_combine(const float* y, int splits, const int32_t* pos, const float* top
   MOE_TRY(check_ptr(out, "out"));
   if (splits < 1) return fail(MOE_ERR_INVALID, "splits must be >= 1");
   if (T == 0) return MOE_OK;
-  MOE_HIP(moe::launch_combine(y, splits, (size_t)T * k * d, pos, topk_w, pad_mask, out, T, d, k,
+  MOE_HIP(moe::launch_combine(y, splits, nullptr, (size_t)T * k * d, pos, topk_w, pad_mask, out, T, d, k,
                               static_cast<hipStream_t>(stream)),
           "combine");
   return MOE_OK;

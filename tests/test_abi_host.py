@@ -86,16 +86,18 @@ def test_stage_entry_points_check_arguments():
 
 
 def test_workspace_size_and_split_policy():
-    # decode shapes split the down projection's contraction; prefill shapes do not
+    # decode shapes split the down projection's contraction to fill the chip
     assert moe.down_splits(8, 6144, 32768, 8, 2) == 8
     assert moe.down_splits(64, 6144, 32768, 8, 2) == 4
-    assert moe.down_splits(65, 6144, 32768, 8, 2) == 1
     assert moe.down_splits(64, 256, 512, 8, 2) == 1
     # narrow f (one GPU's share of 8-way tensor parallelism): split until the chip is filled
     assert moe.down_splits(8, 6144, 4096, 8, 2) == 4
     assert moe.down_splits(8, 1536, 2048, 8, 2) == 2
     assert moe.down_splits(64, 6144, 4096, 8, 2) == 4
     assert moe.down_splits(8192, 6144, 4096, 8, 2) == 1
+    # prefill, long contraction: launched with 2 parts, of which the kernel keeps 1 or 2
+    assert moe.down_splits(8192, 6144, 32768, 8, 2) == 2
+    assert moe.down_splits(65, 256, 8192, 8, 2) == 2
     # the gate/up split's partial sums are part of the decode workspace at narrow f
     assert moe.workspace_bytes(8, 6144, 4096, 8, 2) >= 2 * 4 * 16 * 4096 * 4
     assert moe.workspace_bytes(8, 6144, 32768, 8, 2) < 16 * 32768 * 2 + 8 * 16 * 6144 * 4 + (1 << 20)

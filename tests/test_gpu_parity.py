@@ -365,6 +365,22 @@ def test_layer_at_the_assignment_limit():
     check_layer(inp, d, rows=rows, label="T=2^23 k=2 d=256 f=256")
 
 
+# Prefill with f >= 8192: the down kernel is launched with 2 parts and keeps 1 or 2 on the
+# device (the combine reads its choice). 20 live workgroups under-fill the chip: 2 parts;
+# 16 m-tiles x 16 column tiles = exactly one round of 256: 1 part; all rows padded: 1 part.
+@pytest.mark.parametrize("kw", [dict(T=2048, d=256, f=8192, E=8, k=2, n_pad=17),
+                                dict(T=4096, d=4096, f=8192, E=1, k=1),
+                                dict(T=100, d=256, f=8192, n_pad=100)])
+def test_prefill_down_parts_chosen_on_device(kw):
+    inp, d = small_case("parts", **kw)
+    if kw.get("n_pad") == kw["T"]:  # nothing to compare against: +0.0 everywhere
+        out, _ = run_forward(d, kw["T"], kw["d"], kw["f"], 8, 2)
+        assert np.all(out == 0) and not np.any(np.signbit(out))
+        return
+    rows = sample_rows(kw["T"], 16, seed=5) if kw["T"] * kw["d"] > 1 << 20 else None
+    check_layer(inp, d, rows=rows, label=str(kw))
+
+
 def test_all_tokens_padded():
     inp, d = small_case("allpad", T=32, d=256, f=512, n_pad=32)
     out, dbg = run_forward(d, 32, 256, 512, 8, 2)
