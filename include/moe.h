@@ -101,7 +101,11 @@ int moe_forward_ex(const void* x, const float* router_w, const int8_t* w_gate, c
                    void* workspace, size_t workspace_bytes, const moe_debug_out* dbg);
 
 /* Step 1-2 alone: router logits, softmax and top-k (Guide section 3, MoE steps 1-2).
-   Writes topk_ids int32 [T][k] and topk_w fp32 [T][k]; padded tokens get -1 and 0. */
+   Writes topk_ids int32 [T][k] and topk_w fp32 [T][k]; padded tokens get -1 and 0. A token's
+   logits are summed in one fixed order whatever the batch size, so its ids and weights are
+   the same bits in any batch and in moe_forward. At T <= 64 with E = 8 the per-group partial
+   sums live in the library workspace, which this call may allocate (MOE_ERR_NOMEM if it
+   cannot) and which overlapping calls share. */
 int moe_route(const void* x, const float* router_w, const float* router_bias,
               const uint8_t* pad_mask, int32_t* topk_ids, float* topk_w, int T, int d, int E,
               int k, void* stream);
@@ -132,7 +136,9 @@ int moe_gate_up(const void* x, const int32_t* perm, const int32_t* offsets, cons
 /* Step 3, second half: y = h (q_down[e] * s_down[e]) for the rows of every expert segment,
    with the contraction over f cut into `splits` equal parts: y fp32 [splits][T*k][d] holds
    one partial sum per part (their sum, in part order, is the result). splits must divide
-   f / 128. moe_down_splits() gives the count moe_forward uses for a shape. */
+   f / 128. moe_down_splits() gives the count moe_forward launches with for a shape; at
+   T > 64 moe_forward's own down launch may then keep 1 of those 2 parts, which its combine
+   learns on the device (this entry point always writes exactly `splits`). */
 int moe_down(const void* h, const int32_t* offsets, const int8_t* w_down, const void* scales,
              float* y, int splits, int T, int d, int f, int E, int k, void* stream);
 int moe_down_splits(int T, int d, int f, int E, int k);
