@@ -290,6 +290,34 @@ def test_down_stage_parity(name):
     assert n <= s.T * s.k
 
 
+@pytest.mark.parametrize("kw", [dict(T=8, d=1024, f=2048), dict(T=64, d=768, f=4096, n_pad=9),
+                                dict(T=40, d=1536, f=1024, n_pad=3)])
+def test_forward_equals_its_stages_bitwise(kw):
+    # moe_forward at T <= 64 routes in two launches and combines inside the down launch; the
+    # stage entry points run each step on its own. Same arithmetic in the same order: the
+    # outputs must be the same bits.
+    inp, d = small_case("stages", **kw)
+    T, dd, f, E, k = kw["T"], kw["d"], kw["f"], 8, 2
+    out, _ = run_forward(d, T, dd, f, E, k)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    pos = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    h = torch.empty((T * k, f), dtype=torch.float16, device="cuda")
+    splits = moe.down_splits(T, dd, f, E, k)
+    y = torch.empty((splits, T * k, dd), dtype=torch.float32, device="cuda")
+    staged = torch.full((T, dd), float("nan"), device="cuda")
+    moe.moe_route(d["x"], d["router_w"], d["router_bias"], d["pad_mask"], ids, w, T, dd, E, k)
+    moe.moe_dispatch(ids, d["pad_mask"], counts, offsets, perm, pos, T, E, k)
+    moe.moe_gate_up(d["x"], perm, offsets, d["w_gate"], d["w_up"], d["scales"], h, T, dd, f, E, k)
+    moe.moe_down(h, offsets, d["w_down"], d["scales"], y, splits, T, dd, f, E, k)
+    moe.moe_combine(y, splits, pos, w, d["pad_mask"], staged, T, dd, k)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.view(np.uint32), staged.cpu().numpy().view(np.uint32))
+
+
 def test_combine_stage():
     rng = np.random.default_rng(3)
     T, dd, k, splits = 37, 512, 2, 3
