@@ -72,7 +72,9 @@ def test_dense_onehot_formulation(case):
 
 # ------------------------------------------------------------------------ graph-captured forward
 
-@pytest.mark.parametrize("case", ["tiny", "decode", dict(T=200, d=256, f=512, n_pad=10)])
+# the last case runs the prefill down kernel that picks its number of parts on the device
+@pytest.mark.parametrize("case", ["tiny", "decode", dict(T=200, d=256, f=512, n_pad=10),
+                                  dict(T=1500, d=256, f=8192, n_pad=20)])
 def test_graph_replays_match_eager(case):
     s, inp, d = grok_case(case) if isinstance(case, str) else small("graph", **case)
     ws = torch.empty(moe.workspace_bytes(s.T, s.d, s.f, s.E, s.k) + 256, dtype=torch.uint8, device="cuda")
