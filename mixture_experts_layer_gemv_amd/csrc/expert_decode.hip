@@ -235,7 +235,7 @@ __global__ __launch_bounds__(128) void gate_up_decode_kernel(
 // ------------------------------------------------------------------------------------
 // The GeGLU epilogue of a split gate/up contraction: for row r < offsets[E] (expert e),
 // g = s_g * (sum over parts p in order of P[2p][r]), u likewise from P[2p + 1]; H[r] =
-// fp16(gelu_tanh(g) * u). grid (rows_cap), block 256, 8 columns per thread and step.
+// fp16(gelu_tanh(g) * u). grid (rows_cap, ceil(f / 2048)), block 256, 8 columns per thread.
 __global__ __launch_bounds__(256) void geglu_finish_kernel(const float* __restrict__ P,
                                                            const int32_t* __restrict__ offsets,
                                                            const uint16_t* __restrict__ scales,
@@ -247,7 +247,8 @@ __global__ __launch_bounds__(256) void geglu_finish_kernel(const float* __restri
   while (e + 1 < E && offsets[e + 1] <= r) ++e;
   const uint16_t* sc = scales + (size_t)e * (2 * (size_t)f + d);
   const size_t plane = (size_t)rows_cap * f;
-  for (int n = 8 * threadIdx.x; n < f; n += 8 * 256) {
+  const int n = 2048 * blockIdx.y + 8 * threadIdx.x;
+  if (n < f) {
     f32x4 g[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     f32x4 u[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     for (int p = 0; p < parts; ++p) {
@@ -337,8 +338,8 @@ hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* perm, const i
                          w_up, scales, H, P, d, f, rows_cap);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(geglu_finish_kernel, dim3(rows_cap), dim3(256), 0, stream, P, offsets, scales, H, parts, d,
-                       f, E, rows_cap);
+    hipLaunchKernelGGL(geglu_finish_kernel, dim3(rows_cap, (f + 2047) / 2048), dim3(256), 0, stream, P, offsets,
+                       scales, H, parts, d, f, E, rows_cap);
   } else if (T <= 16) {
     hipLaunchKernelGGL((gate_up_decode_kernel<1, 4, false>), grid, block, 0, stream, x, perm, offsets, w_gate,
                        w_up, scales, H, P, d, f, rows_cap);

@@ -5,6 +5,8 @@
 // kernel splits to fill a ragged last round of workgroups.
 #pragma once
 
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace moe {
@@ -17,9 +19,10 @@ namespace moe {
 // Large batches: the most parts the prefill down kernel may use. Launched with 2, it keeps
 // 1 or 2 on the device (from the live tile count, which only the device knows) and reports
 // the choice to the combine.
-inline int down_splits(int T, int d, int f, int E) {
+// The slab counts take the experts a batch can touch, min(E, T * k): at T = 1 only two stream.
+inline int down_splits(int T, int d, int f, int E, int k) {
   if (T > kDecodeMaxT) return f >= 8192 ? 2 : 1;
-  const long slabs = (long)(d / 256) * E;
+  const long slabs = (long)(d / 256) * std::min<long>(E, (long)T * k);
   const long target = T <= 16 ? 1024 : 512;
   int s = 1;
   while (s < 8 && slabs * s < target && f / (2 * s) >= 1024 && (f / 128) % (2 * s) == 0) s *= 2;
@@ -27,9 +30,9 @@ inline int down_splits(int T, int d, int f, int E) {
 }
 
 // gate/up: about 512 workgroups, parts of at least 768 rows of the contraction over d.
-inline int gate_up_parts(int T, int d, int f, int E) {
+inline int gate_up_parts(int T, int d, int f, int E, int k) {
   if (T > kDecodeMaxT) return 1;
-  const long slabs = (long)(f / 256) * E;
+  const long slabs = (long)(f / 256) * std::min<long>(E, (long)T * k);
   int s = 1;
   while (s < 8 && slabs * s < 512 && d / (2 * s) >= 768 && (d / 128) % (2 * s) == 0) s *= 2;
   return s;

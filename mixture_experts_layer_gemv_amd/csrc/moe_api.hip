@@ -86,9 +86,9 @@ Layout make_layout(int T, int d, int f, int E, int k) {
   L.perm = take(tk * 4);
   L.pos = take(tk * 4);
   L.h = take(tk * f * 2);
-  L.splits = down_splits(T, d, f, E);
+  L.splits = down_splits(T, d, f, E, k);
   L.y = take((size_t)L.splits * tk * d * 4);
-  L.gparts = gate_up_parts(T, d, f, E);
+  L.gparts = gate_up_parts(T, d, f, E, k);
   L.gp = L.gparts > 1 ? take((size_t)2 * L.gparts * tk * f * 4) : 0;
   const int nchunks = moe::dispatch_chunks(T);
   L.dchunk = nchunks > 0 ? take((size_t)2 * nchunks * E * 4) : 0;
@@ -232,7 +232,7 @@ size_t moe_workspace_bytes(int T, int d, int f, int E, int k) {
 
 int moe_down_splits(int T, int d, int f, int E, int k) {
   if (check_shape(T, d, f, E, k) != MOE_OK) return 0;
-  return down_splits(T, d, f, E);
+  return down_splits(T, d, f, E, k);
 }
 
 void moe_release_workspace(void) {
@@ -491,7 +491,7 @@ int moe_gate_up(const void* x, const int32_t* perm, const int32_t* offsets, cons
   if (T <= moe::kDecodeMaxT) {
     // the same split of the contraction as moe_forward; its partial sums live in the
     // library workspace
-    const int parts = gate_up_parts(T, d, f, E);
+    const int parts = gate_up_parts(T, d, f, E, k);
     char* gp = nullptr;
     if (parts > 1) MOE_TRY(library_workspace((size_t)2 * parts * T * k * f * 4, &gp));
     MOE_HIP(moe::launch_gate_up_decode(xb, perm, offsets, w_gate, w_up, sc, hh, reinterpret_cast<float*>(gp), parts,

@@ -95,6 +95,9 @@ def test_workspace_size_and_split_policy():
     assert moe.down_splits(8, 1536, 2048, 8, 2) == 2
     assert moe.down_splits(64, 6144, 4096, 8, 2) == 4
     assert moe.down_splits(8192, 6144, 4096, 8, 2) == 1
+    # the policy counts the experts a batch can reach, min(E, T * k)
+    assert moe.down_splits(1, 6144, 4096, 8, 2) == 4
+    assert moe.workspace_bytes(1, 6144, 4096, 8, 2) >= 2 * 8 * 2 * 4096 * 4  # 8 gate/up parts
     # prefill, long contraction: launched with 2 parts, of which the kernel keeps 1 or 2
     assert moe.down_splits(8192, 6144, 32768, 8, 2) == 2
     assert moe.down_splits(65, 256, 8192, 8, 2) == 2

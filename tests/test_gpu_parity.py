@@ -375,6 +375,9 @@ def small_case(name, **kw):
     dict(T=8, d=3072, f=1024, E=8, k=2, scale_jitter=True),
     dict(T=40, d=6144, f=512, E=8, k=2, n_pad=4),
     dict(T=8, d=1536, f=2048, E=8, k=2, x_dist="student4"),
+    # one or two tokens reach at most 2 or 4 experts: the gate/up contraction split in 8 parts
+    dict(T=1, d=6144, f=1024, E=8, k=2),
+    dict(T=2, d=3072, f=512, E=8, k=2, scale_jitter=True),
 ])
 def test_layer_edge_shapes(kw):
     inp, d = small_case("edge", **kw)
