@@ -411,8 +411,9 @@ hipError_t launch_down_prefill(const _Float16* H, const int32_t* offsets, const 
                                int f, int E, int* splits_used, hipStream_t stream) {
   if (splits_used != nullptr && splits != 2) return hipErrorInvalidValue;
   const int nslots = prefill_mslots(rows_cap, E), ntiles = d / (2 * HALF);
-  // H can exceed the last-level cache: split the XCDs 2 (rows) x 4 (columns)
-  const TileOrder order = make_order(nslots, ntiles, 4);
+  // every XCD takes its own weight columns, as for gate/up (measured against 2 x 4 and 4 x 2
+  // XCD grids: equal at 8192 tokens, 2.6% faster on a skewed 4096-token batch)
+  const TileOrder order = make_order(nslots, ntiles, 8);
   dim3 grid(nslots * ntiles, 1, splits);
   hipLaunchKernelGGL(expert_prefill_kernel<false>, grid, dim3(kThreads), 0, stream,
                      reinterpret_cast<const uint16_t*>(H), (const int32_t*)nullptr, offsets, w_down,
