@@ -128,7 +128,7 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}, "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE {world}). The layer would shard over f with one all-reduce of the output; "
               "that path is not built.", file=sys.stderr, flush=True)
         return 2
