@@ -46,7 +46,9 @@ def sparse_out(d, s):
 
 # ------------------------------------------------------------------------ dense one-hot formulation
 
-@pytest.mark.parametrize("case", ["tiny", "decode", dict(T=300, d=256, f=512, n_pad=30), dict(T=40, d=256, f=256, E=4, k=3)])
+# the last case runs the prefill down launch that keeps 1 or 2 parts on the device
+@pytest.mark.parametrize("case", ["tiny", "decode", dict(T=300, d=256, f=512, n_pad=30), dict(T=40, d=256, f=256, E=4, k=3),
+                                  dict(T=200, d=256, f=8192, n_pad=9)])
 def test_dense_onehot_formulation(case):
     s, inp, d = grok_case(case) if isinstance(case, str) else small("dense", **case)
     out = torch.full((s.T, s.d), float("nan"), device="cuda")
@@ -154,8 +156,11 @@ def block_case(s, inp, d, rows):
 # below 1024 tokens the post-norm combine takes two launches over (token, 1024-column chunk)
 # workgroups, from 1024 one workgroup per token (and the router 8 tokens per workgroup);
 # d = 1280 leaves a partial last chunk
+# f = 8192 at T > 64: the down launch keeps 1 or 2 parts on the device and the post-norm
+# combine reads the count there (both combine forms)
 @pytest.mark.parametrize("case", ["tiny", "decode", "batched_decode", dict(T=500, d=256, f=512, n_pad=40),
-                                  dict(T=40, d=1280, f=256, n_pad=5), dict(T=1100, d=1280, f=256, n_pad=60)])
+                                  dict(T=40, d=1280, f=256, n_pad=5), dict(T=1100, d=1280, f=256, n_pad=60),
+                                  dict(T=300, d=256, f=8192, n_pad=11), dict(T=1100, d=256, f=8192, n_pad=7)])
 def test_block_parity(case):
     s, inp, d = grok_case(case) if isinstance(case, str) else small("block", **case)
     rows = np.arange(s.T) if s.T * s.d <= 200_000 else sample_rows(s.T, 12, seed=4)
