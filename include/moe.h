@@ -126,7 +126,7 @@ int moe_dispatch(const int32_t* topk_ids, const uint8_t* pad_mask, int32_t* coun
    segment take x[perm[r]]; g, u = that row times the dequantised gate / up matrices
    (fp32 accumulation, per-output-channel scales applied in fp32); h = gelu_tanh(g) * u,
    stored as fp16 in h [T*k][f] at row r. Rows at or beyond offsets[E] are not written.
-   At T <= 64 with narrow f (too few 256-column slabs to fill the chip) the contraction over
+   At T <= 160 with narrow f (too few 256-column slabs to fill the chip) the contraction over
    d is split as in moe_forward; the partial sums then live in the library workspace, which
    this call may allocate (MOE_ERR_NOMEM if it cannot) and which overlapping calls share. */
 int moe_gate_up(const void* x, const int32_t* perm, const int32_t* offsets, const int8_t* w_gate,
@@ -137,7 +137,7 @@ int moe_gate_up(const void* x, const int32_t* perm, const int32_t* offsets, cons
    with the contraction over f cut into `splits` equal parts: y fp32 [splits][T*k][d] holds
    one partial sum per part (their sum, in part order, is the result). splits must divide
    f / 128. moe_down_splits() gives the count moe_forward launches with for a shape; at
-   T > 64 moe_forward's own down launch may then keep 1 of those 2 parts, which its combine
+   T > 160 moe_forward's own down launch may then keep 1 of those 2 parts, which its combine
    learns on the device (this entry point always writes exactly `splits`). */
 int moe_down(const void* h, const int32_t* offsets, const int8_t* w_down, const void* scales,
              float* y, int splits, int T, int d, int f, int E, int k, void* stream);

@@ -20,8 +20,8 @@
 // after the contraction. Loads run kStages - 1 steps ahead of the MFMAs (register ring).
 //
 // Rows: an expert's segment of the dispatch has M rows (M <= T). A pass covers MT
-// 16-row MFMA tiles (MT = 1 when T <= 16, else 2);
-// longer segments take further passes over the weights.
+// 16-row MFMA tiles (MT = 1 when T <= 16, 2 when T <= 64, else 3, the most the registers
+// hold); longer segments take further passes over the weights.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -333,8 +333,11 @@ hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* perm, const i
     if (T <= 16)
       hipLaunchKernelGGL((gate_up_decode_kernel<1, 4, true>), grid, block, 0, stream, x, perm, offsets, w_gate,
                          w_up, scales, H, P, d, f, rows_cap);
-    else
+    else if (T <= 64)
       hipLaunchKernelGGL((gate_up_decode_kernel<2, 3, true>), grid, block, 0, stream, x, perm, offsets, w_gate,
+                         w_up, scales, H, P, d, f, rows_cap);
+    else
+      hipLaunchKernelGGL((gate_up_decode_kernel<3, 3, true>), grid, block, 0, stream, x, perm, offsets, w_gate,
                          w_up, scales, H, P, d, f, rows_cap);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -343,8 +346,11 @@ hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* perm, const i
   } else if (T <= 16) {
     hipLaunchKernelGGL((gate_up_decode_kernel<1, 4, false>), grid, block, 0, stream, x, perm, offsets, w_gate,
                        w_up, scales, H, P, d, f, rows_cap);
-  } else {
+  } else if (T <= 64) {
     hipLaunchKernelGGL((gate_up_decode_kernel<2, 3, false>), grid, block, 0, stream, x, perm, offsets, w_gate,
+                       w_up, scales, H, P, d, f, rows_cap);
+  } else {
+    hipLaunchKernelGGL((gate_up_decode_kernel<3, 3, false>), grid, block, 0, stream, x, perm, offsets, w_gate,
                        w_up, scales, H, P, d, f, rows_cap);
   }
   return hipGetLastError();
@@ -357,8 +363,11 @@ hipError_t launch_down_decode(const _Float16* H, const int32_t* offsets, const i
   if (T <= 16)
     hipLaunchKernelGGL((down_decode_kernel<1, 3>), grid, block, 0, stream, H, offsets, w_down, scales, Y, d,
                        f, rows_cap);
-  else
+  else if (T <= 64)
     hipLaunchKernelGGL((down_decode_kernel<2, 4>), grid, block, 0, stream, H, offsets, w_down, scales, Y, d,
+                       f, rows_cap);
+  else
+    hipLaunchKernelGGL((down_decode_kernel<3, 3>), grid, block, 0, stream, H, offsets, w_down, scales, Y, d,
                        f, rows_cap);
   return hipGetLastError();
 }

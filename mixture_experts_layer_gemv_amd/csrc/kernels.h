@@ -7,13 +7,14 @@
 
 namespace moe {
 
-// T at or below which the expert FFN takes the weight-streaming (decode) kernels.
-constexpr int kDecodeMaxT = 64;
+// T at or below which the expert FFN takes the weight-streaming (decode) kernels: they read
+// each touched expert's weights once per pass of up to 16 (T <= 16), 32 (T <= 64) or 48 rows.
+constexpr int kDecodeMaxT = 160;
 
 // T at or below which routing with E == 8 can run in two launches: router_partial_kernel
 // (group sums, fp32 [T][d / 128][8]) and route_finish_kernel (sums, softmax, top-k, and
 // optionally the dispatch).
-constexpr int kRouterSplitMaxT = kDecodeMaxT;
+constexpr int kRouterSplitMaxT = 64;
 // floats of the group-sum scratch for (T, d, E); 0 where the two-launch routing does not apply
 size_t router_partial_floats(int T, int d, int E);
 hipError_t launch_router_partial(const uint16_t* x, const float* router_w, float* partial, int T, int d,

@@ -100,7 +100,9 @@ def test_workspace_size_and_split_policy():
     assert moe.workspace_bytes(1, 6144, 4096, 8, 2) >= 2 * 8 * 2 * 4096 * 4  # 8 gate/up parts
     # prefill, long contraction: launched with 2 parts, of which the kernel keeps 1 or 2
     assert moe.down_splits(8192, 6144, 32768, 8, 2) == 2
-    assert moe.down_splits(65, 256, 8192, 8, 2) == 2
+    assert moe.down_splits(161, 256, 8192, 8, 2) == 2
+    # up to 160 tokens the streaming kernels run, with the small-batch policy
+    assert moe.down_splits(160, 256, 8192, 8, 2) == 8
     # the gate/up split's partial sums are part of the decode workspace at narrow f
     assert moe.workspace_bytes(8, 6144, 4096, 8, 2) >= 2 * 4 * 16 * 4096 * 4
     assert moe.workspace_bytes(8, 6144, 32768, 8, 2) < 16 * 32768 * 2 + 8 * 16 * 6144 * 4 + (1 << 20)

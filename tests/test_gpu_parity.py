@@ -143,9 +143,9 @@ def test_router_is_batch_invariant_bitwise(dd):
 
 @pytest.mark.parametrize("T", [12, 40])
 def test_forward_routing_matches_route_bitwise(T):
-    # moe_forward at T <= 64 finishes the routing inside the dispatch launch (at T <= 16 all of
-    # it in one workgroup): its ids and weights are those of moe_route on the same rows, bit
-    # for bit
+    # moe_forward at T <= 64 finishes the routing inside the dispatch launch: its ids and
+    # weights are those of moe_route on the same rows (one workgroup per token there), bit for
+    # bit
     s = synth.custom("fwd_route", T=100, d=1024, f=256, n_pad=7, bias=(0.2, 0, 0, 0, 0, 0, -0.1, 0))
     inp = synth.make_inputs(s)
     d = to_dev(inp)
@@ -295,9 +295,9 @@ def test_down_stage_parity(name):
 @pytest.mark.parametrize("kw", [dict(T=8, d=1024, f=2048), dict(T=64, d=768, f=4096, n_pad=9),
                                 dict(T=40, d=1536, f=1024, n_pad=3)])
 def test_forward_equals_its_stages_bitwise(kw):
-    # moe_forward at T <= 64 routes in two launches and combines inside the down launch; the
-    # stage entry points run each step on its own. Same arithmetic in the same order: the
-    # outputs must be the same bits.
+    # moe_forward at T <= 64 routes in two launches (group sums, then routing with the
+    # dispatch); the stage entry points run each step on its own. Same arithmetic in the same
+    # order: the outputs must be the same bits.
     inp, d = small_case("stages", **kw)
     T, dd, f, E, k = kw["T"], kw["d"], kw["f"], 8, 2
     out, _ = run_forward(d, T, dd, f, E, k)
@@ -380,6 +380,10 @@ def small_case(name, **kw):
     # one or two tokens reach at most 2 or 4 experts: the gate/up contraction split in 8 parts
     dict(T=1, d=6144, f=1024, E=8, k=2),
     dict(T=2, d=3072, f=512, E=8, k=2, scale_jitter=True),
+    # 65..160 tokens: the streaming kernels in 48-row passes; with the gate/up split (narrow f),
+    # and with a biased router that sends one expert over 48 rows (several passes)
+    dict(T=100, d=6144, f=1024, E=8, k=2, n_pad=6),
+    dict(T=160, d=256, f=512, E=8, k=2, bias=(3.0, 2.0, 0, 0, 0, 0, 0, 0)),
 ])
 def test_layer_edge_shapes(kw):
     inp, d = small_case("edge", **kw)
@@ -403,7 +407,7 @@ def test_layer_at_the_assignment_limit():
 # 16 m-tiles x 16 column tiles = exactly one round of 256: 1 part; all rows padded: 1 part.
 @pytest.mark.parametrize("kw", [dict(T=2048, d=256, f=8192, E=8, k=2, n_pad=17),
                                 dict(T=4096, d=4096, f=8192, E=1, k=1),
-                                dict(T=100, d=256, f=8192, n_pad=100)])
+                                dict(T=300, d=256, f=8192, n_pad=300)])
 def test_prefill_down_parts_chosen_on_device(kw):
     inp, d = small_case("parts", **kw)
     if kw.get("n_pad") == kw["T"]:  # nothing to compare against: +0.0 everywhere
@@ -506,17 +510,19 @@ def test_doubling_down_scales_doubles_out_exactly(T):
     assert np.max(np.abs(b - 2 * a)) <= 1e-3 * rms(2 * a)
 
 
-def test_decode_and_prefill_kernels_agree():
-    # 64 tokens take the streaming kernels; the same tokens plus one padded token take the
-    # tiled ones; the real rows must agree to the output tolerance
-    inp, d = small_case("paths", T=65, d=512, f=768, n_pad=0)
-    inp64 = {n: (v[:64] if n == "x" else v) for n, v in inp.items()}
-    a, _ = run_forward(dict(d, x=d["x"][:64].contiguous()), 64, 512, 768, 8, 2)
-    pad = torch.ones(65, dtype=torch.uint8, device="cuda")
-    pad[64] = 0
-    b, _ = run_forward(dict(d, pad_mask=pad), 65, 512, 768, 8, 2)
-    assert np.max(np.abs(a - b[:64])) <= 1e-3 * rms(a)
-    del inp64
+@pytest.mark.parametrize("T", [64, 160])
+def test_kernel_paths_agree_across_a_boundary(T):
+    # T tokens, then the same tokens plus one padded token. At 64 | 65 the streaming kernels
+    # go from 32- to 48-row passes (each row's MFMA sequence is unchanged: the same bits); at
+    # 160 | 161 the tiled kernels take over (the real rows agree to the output tolerance)
+    inp, d = small_case("paths", T=T + 1, d=512, f=768, n_pad=0)
+    a, _ = run_forward(dict(d, x=d["x"][:T].contiguous()), T, 512, 768, 8, 2)
+    pad = torch.ones(T + 1, dtype=torch.uint8, device="cuda")
+    pad[T] = 0
+    b, _ = run_forward(dict(d, pad_mask=pad), T + 1, 512, 768, 8, 2)
+    if T == 64:
+        assert np.array_equal(a, b[:T])
+    assert np.max(np.abs(a - b[:T])) <= 1e-3 * rms(a)
 
 
 def test_caller_workspace_matches_library_workspace():

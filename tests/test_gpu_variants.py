@@ -156,7 +156,7 @@ def block_case(s, inp, d, rows):
 # below 1024 tokens the post-norm combine takes two launches over (token, 1024-column chunk)
 # workgroups, from 1024 one workgroup per token (and the router 8 tokens per workgroup);
 # d = 1280 leaves a partial last chunk
-# f = 8192 at T > 64: the down launch keeps 1 or 2 parts on the device and the post-norm
+# f = 8192 at T > 160: the down launch keeps 1 or 2 parts on the device and the post-norm
 # combine reads the count there (both combine forms)
 @pytest.mark.parametrize("case", ["tiny", "decode", "batched_decode", dict(T=500, d=256, f=512, n_pad=40),
                                   dict(T=40, d=1280, f=256, n_pad=5), dict(T=1100, d=1280, f=256, n_pad=60),
