@@ -1,4 +1,4 @@
-// Expert FFN for large batches (T > 64): grouped W8A16 GEMMs on the MFMA units.
+// Expert FFN for large batches (T > 160): grouped W8A16 GEMMs on the MFMA units.
 // (Grok-1 Admin & Architecture Guide, section 3, MoE step 3, the gated GeLU expert
 // gelu(linear(x)) * linear_v(x) -> linear_1; "Quantized weights": int8 weights
 // dequantised as q * s with one scale per output channel, compute in bf16.)
@@ -18,6 +18,9 @@
 //     workgroup, on the way into LDS, and stored transposed ([column][k]), so every MFMA
 //     operand is one 16-byte LDS read; column 2 c + q of a 64-column group goes to LDS
 //     row 32 q + c, which gives each lane 2 adjacent output columns in the epilogue.
+// Batches whose experts average at most 96 rows use 128-row tiles (half the activation
+// loads and LDS stores per slice; wavefronts 4-7 only move slices), and a tile of at most 64
+// rows spreads its 32x32 MFMA tiles over all 8 wavefronts so that all 4 SIMDs multiply.
 // Rows are gathered through the dispatch permutation (gate/up) or read in segment order
 // (down). Tiles are assigned on the device: m-slots enumerate the m-tiles of all expert
 // segments in expert order (read from offsets), surplus slots exit at once; the order of
@@ -31,7 +34,7 @@
 namespace moe {
 
 namespace {
-constexpr int BM = 256;         // rows per workgroup tile
+constexpr int BM = 256;         // rows per workgroup tile (LDS is sized for it; a launch may use 128)
 constexpr int BK = 64;          // contraction depth per slice
 constexpr int HALF = 128;       // columns per weight half-tile
 constexpr int LDS_LD = BK + 8;  // 16-bit elements per LDS row (16-byte pad)
@@ -62,17 +65,17 @@ struct Mfma32<f16x8> {
   }
 };
 
-// (expert, first row, rows) of m-slot `slot`, or false when the slot is surplus.
-__device__ __forceinline__ bool find_tile(const int32_t* offsets, int E, int slot, int& e, int& row0,
+// (expert, first row, rows) of m-slot `slot` with bm-row tiles, or false when the slot is surplus.
+__device__ __forceinline__ bool find_tile(const int32_t* offsets, int E, int slot, int bm, int& e, int& row0,
                                           int& rows) {
   int s = slot;
   for (int ee = 0; ee < E; ++ee) {
     const int M = offsets[ee + 1] - offsets[ee];
-    const int nt = (M + BM - 1) / BM;
+    const int nt = (M + bm - 1) / bm;
     if (s < nt) {
       e = ee;
-      row0 = offsets[ee] + s * BM;
-      rows = min(BM, M - s * BM);
+      row0 = offsets[ee] + s * bm;
+      rows = min(bm, M - s * bm);
       return true;
     }
     s -= nt;
@@ -137,16 +140,17 @@ __device__ __forceinline__ void tile_of(int w, const TileOrder& o, int& mslot, i
 // rounds of ncu (one per CU); two parts fill a ragged last round better but cost a second fp32
 // partial, 8 bytes per output element (written, then read by the combine) at about 5 TB/s
 // against 2 f FLOPs at about 1 PFLOP/s, i.e. about 800 / f of the kernel's time.
-__device__ __forceinline__ int down_parts(const int32_t* offsets, int E, int ntiles, int ncu, int f) {
+__device__ __forceinline__ int down_parts(const int32_t* offsets, int E, int bm, int ntiles, int ncu, int f) {
   int live = 0;
-  for (int e = 0; e < E; ++e) live += (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+  for (int e = 0; e < E; ++e) live += (offsets[e + 1] - offsets[e] + bm - 1) / bm;
   if (live == 0) return 1;
   const float r1 = (float)(live * ntiles) / (float)ncu, r2 = 2.0f * r1;
   const float fill1 = ceilf(r1) / r1, fill2 = ceilf(r2) / r2;
   return fill1 > fill2 + 800.0f / (float)f ? 2 : 1;
 }
 
-template <bool kGateUp>
+// kBM: rows per tile, 256 or 128.
+template <bool kGateUp, int kBM>
 __global__ __launch_bounds__(kThreads) void expert_prefill_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, const int8_t* __restrict__ B0,
@@ -157,14 +161,14 @@ __global__ __launch_bounds__(kThreads) void expert_prefill_kernel(
 
   int parts = gridDim.z;
   if (!kGateUp && splits_used != nullptr) {  // launched with 2 parts: keep 1 or 2
-    parts = down_parts(offsets, E, order.ntiles, order.ncu, f);
+    parts = down_parts(offsets, E, kBM, order.ntiles, order.ncu, f);
     if (blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x == 0) *splits_used = parts;
     if ((int)blockIdx.z >= parts) return;
   }
   int mslot, ntile;
   tile_of(blockIdx.x, order, mslot, ntile);
   int e, row0, rows;
-  if (!find_tile(offsets, E, mslot, e, row0, rows)) return;
+  if (!find_tile(offsets, E, mslot, kBM, e, row0, rows)) return;
 
   const int K = kGateUp ? d : f;  // contraction length
   const int N = kGateUp ? f : d;  // columns of each weight matrix
@@ -176,10 +180,11 @@ __global__ __launch_bounds__(kThreads) void expert_prefill_kernel(
   const int wm = wave >> 1, wn = wave & 1;  // 4 x 2 wavefronts, 64 rows x 128 columns each
 
   // ---- global -> register loads of one slice
-  // A: rows tid / 8 + 64 i (i = 0..3), 16-byte chunk tid % 8 of the slice
-  const uint16_t* arow[4];
+  // A: rows tid / 8 + 64 i (i < kBM / 64), 16-byte chunk tid % 8 of the slice
+  constexpr int kArows = kBM / 64;
+  const uint16_t* arow[kArows];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kArows; ++i) {
     const int m = min(tid / 8 + 64 * i, rows - 1);  // rows past the tile end repeat a live row
     const size_t src_row = kGateUp ? (size_t)perm[row0 + m] : (size_t)(row0 + m);
     arow[i] = A + src_row * K + kbeg + 8 * (tid % 8);
@@ -199,12 +204,12 @@ __global__ __launch_bounds__(kThreads) void expert_prefill_kernel(
 
   // two register stages: the loads of slices i + 1 and i + 2 are in flight while slice i
   // is multiplied out of LDS
-  u32x4 ra[2][4];
+  u32x4 ra[2][kArows];
   uint32_t rb[2][8];
   auto gload = [&](auto stage, int kk) {
     constexpr int rs = decltype(stage)::value;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ra[rs][i] = *reinterpret_cast<const u32x4*>(arow[i] + kk);
+    for (int i = 0; i < kArows; ++i) ra[rs][i] = *reinterpret_cast<const u32x4*>(arow[i] + kk);
     const uint32_t sbase = (uint32_t)(kbeg + kk) * ldb;
 #pragma unroll
     for (int r = 0; r < 8; ++r) rb[rs][r] = __builtin_amdgcn_raw_buffer_load_b32(br, bvoff, sbase + r * ldb, 0);
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void expert_prefill_kernel(
     uint16_t* sA = st;
     uint16_t* sB = st + A_ELEMS;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kArows; ++i)
       *reinterpret_cast<u32x4*>(sA + (size_t)(tid / 8 + 64 * i) * LDS_LD + 8 * (tid % 8)) = ra[rs][i];
     store_col<kGateUp, 0>(sB, hb * HALF + brow + 0, 8 * kg, rb[rs]);
     store_col<kGateUp, 1>(sB, hb * HALF + brow + 32, 8 * kg, rb[rs]);
@@ -296,6 +301,93 @@ __global__ __launch_bounds__(kThreads) void expert_prefill_kernel(
   gload(R1, min(BK, klast));
   lds_store(R0, L0);
   __syncthreads();
+  if constexpr (kBM == 128) {
+    if (rows <= 64) {  // uniform per workgroup
+      // Tiles of at most 64 rows: the same 32x32 MFMA tiles (so the same sums, bit for bit),
+      // spread over all 8 wavefronts instead of the 2 of row group 0, so that all 4 SIMDs
+      // multiply. Wavefront w takes row tile w / 4 and column pair c = w % 4:
+      //   gate/up: gate and up tiles at LDS rows (c / 2) * 64 + 32 (c % 2) (+ 128 for up),
+      //            i.e. column 2 (lane % 32) + c % 2 of 64-column group c / 2;
+      //   down:    LDS rows (c / 2) * 128 + (c % 2) * 64 + 32 q (q = 0, 1), i.e. columns
+      //            2 (lane % 32) + q of that group.
+      const int nm = wave >> 2, c = wave & 3;
+      int nbro[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        nbro[j] = (kGateUp ? j * HALF + (c >> 1) * 64 + 32 * (c & 1) : (c >> 1) * HALF + (c & 1) * 64 + 32 * j) +
+                  (lane & 31);
+      const int narl = 32 * nm + (lane & 31);
+      f32x16 accn[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) accn[j][i] = 0.0f;
+      Frag na[2], nb[2][2];
+      auto read_n = [&](const uint16_t* st, int buf, int ks) {
+        na[buf] = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(st + (size_t)narl * LDS_LD + ks + kq));
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          nb[buf][j] =
+              __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(st + A_ELEMS + (size_t)nbro[j] * LDS_LD + ks + kq));
+      };
+      auto slice_n = [&](const uint16_t* cur) {
+        read_n(cur, 0, 0);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+          if (kk + 1 < BK / 16) read_n(cur, (kk + 1) & 1, (kk + 1) * 16);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) accn[j] = Mfma32<Frag>::run(na[kk & 1], nb[kk & 1][j], accn[j]);
+        }
+      };
+      if (__builtin_amdgcn_readfirstlane(nm * 32 < rows ? 1 : 0)) {  // uniform per wavefront
+        for (int it = 0; it < nslices; it += 2) {
+          gload(R0, min((it + 2) * BK, klast));
+          slice_n(L0);
+          lds_store(R1, L1);
+          __syncthreads();
+          gload(R1, min((it + 3) * BK, klast));
+          slice_n(L1);
+          lds_store(R0, L0);
+          __syncthreads();
+        }
+      } else {
+        for (int it = 0; it < nslices; it += 2) {
+          gload(R0, min((it + 2) * BK, klast));
+          lds_store(R1, L1);
+          __syncthreads();
+          gload(R1, min((it + 3) * BK, klast));
+          lds_store(R0, L0);
+          __syncthreads();
+        }
+      }
+      const uint16_t* sc = scales + (size_t)e * (2 * (size_t)f + d);
+      const int rq = 4 * (lane >> 5);
+      if constexpr (kGateUp) {
+        const int n = n0 + (c >> 1) * 64 + 2 * (lane & 31) + (c & 1);
+        const float sg = bf16_bits_to_float(sc[n]), su = bf16_bits_to_float(sc[f + n]);
+        _Float16* H = reinterpret_cast<_Float16*>(out);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = 32 * nm + 8 * (i >> 2) + rq + (i & 3);
+          if (m < rows) H[(size_t)(row0 + m) * f + n] = (_Float16)(gelu_tanh(accn[0][i] * sg) * (accn[1][i] * su));
+        }
+      } else {
+        float* Y = reinterpret_cast<float*>(out) + (size_t)blockIdx.z * rows_cap * d;
+        const int n = n0 + (c >> 1) * HALF + (c & 1) * 64 + 2 * (lane & 31);
+        const uint32_t s2 = *reinterpret_cast<const uint32_t*>(sc + 2 * (size_t)f + n);
+        const float sd0 = bf16_bits_to_float(s2 & 0xFFFFu), sd1 = bf16_bits_to_float(s2 >> 16);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = 32 * nm + 8 * (i >> 2) + rq + (i & 3);
+          if (m < rows) {
+            u32x2 v = {__float_as_uint(accn[0][i] * sd0), __float_as_uint(accn[1][i] * sd1)};
+            *reinterpret_cast<u32x2*>(Y + (size_t)(row0 + m) * d + n) = v;
+          }
+        }
+      }
+      return;
+    }
+  }
   if (__builtin_amdgcn_readfirstlane(wm * 64 < rows ? 1 : 0)) {  // uniform per wavefront
     for (int it = 0; it < nslices; it += 2) {
       gload(R0, min((it + 2) * BK, klast));
@@ -367,9 +459,13 @@ __global__ __launch_bounds__(kThreads) void expert_prefill_kernel(
   }
 }
 
-// m-slots: enough for every expert segment's m-tiles (sum of ceil(M_e / BM) <= rows / BM
+// m-slots: enough for every expert segment's m-tiles (sum of ceil(M_e / bm) <= rows / bm
 // + E), rounded up to a multiple of the 8 XCDs.
-int prefill_mslots(int rows_cap, int E) { return ((rows_cap + BM - 1) / BM + E + 7) / 8 * 8; }
+int prefill_mslots(int rows_cap, int E, int bm) { return ((rows_cap + bm - 1) / bm + E + 7) / 8 * 8; }
+
+// Tile height: 128 rows while the experts average at most 96 rows (few reach a second
+// 128-row tile), else 256.
+int prefill_bm(int rows_cap, int E) { return rows_cap <= 96 * E ? 128 : 256; }
 
 // xn = n-tile blocks across XCDs (the rest of the 8 split the m-slots), as preferred by
 // the caller when the tile counts allow it; ngroup = n-tiles swept together.
@@ -397,12 +493,14 @@ TileOrder make_order(int nslots, int ntiles, int xn_pref) {
 hipError_t launch_gate_up_prefill(const uint16_t* x, const int32_t* perm, const int32_t* offsets,
                                   const int8_t* w_gate, const int8_t* w_up, const uint16_t* scales,
                                   _Float16* H, int rows_cap, int d, int f, int E, hipStream_t stream) {
-  const int nslots = prefill_mslots(rows_cap, E), ntiles = f / HALF;
+  const int bm = prefill_bm(rows_cap, E);
+  const int nslots = prefill_mslots(rows_cap, E, bm), ntiles = f / HALF;
   // the activations fit the last-level cache: every XCD takes its own weight columns
   const TileOrder order = make_order(nslots, ntiles, 8);
   dim3 grid(nslots * ntiles, 1, 1);
-  hipLaunchKernelGGL(expert_prefill_kernel<true>, grid, dim3(kThreads), 0, stream, x, perm, offsets,
-                     w_gate, w_up, scales, (void*)H, d, f, E, rows_cap, order, (int*)nullptr);
+  auto kern = bm == 128 ? expert_prefill_kernel<true, 128> : expert_prefill_kernel<true, 256>;
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, x, perm, offsets, w_gate, w_up, scales, (void*)H, d,
+                     f, E, rows_cap, order, (int*)nullptr);
   return hipGetLastError();
 }
 
@@ -410,14 +508,16 @@ hipError_t launch_down_prefill(const _Float16* H, const int32_t* offsets, const 
                                const uint16_t* scales, float* Y, int splits, int rows_cap, int d,
                                int f, int E, int* splits_used, hipStream_t stream) {
   if (splits_used != nullptr && splits != 2) return hipErrorInvalidValue;
-  const int nslots = prefill_mslots(rows_cap, E), ntiles = d / (2 * HALF);
+  const int bm = prefill_bm(rows_cap, E);
+  const int nslots = prefill_mslots(rows_cap, E, bm), ntiles = d / (2 * HALF);
   // every XCD takes its own weight columns, as for gate/up (measured against 2 x 4 and 4 x 2
   // XCD grids: equal at 8192 tokens, 2.6% faster on a skewed 4096-token batch)
   const TileOrder order = make_order(nslots, ntiles, 8);
   dim3 grid(nslots * ntiles, 1, splits);
-  hipLaunchKernelGGL(expert_prefill_kernel<false>, grid, dim3(kThreads), 0, stream,
-                     reinterpret_cast<const uint16_t*>(H), (const int32_t*)nullptr, offsets, w_down,
-                     (const int8_t*)nullptr, scales, (void*)Y, d, f, E, rows_cap, order, splits_used);
+  auto kern = bm == 128 ? expert_prefill_kernel<false, 128> : expert_prefill_kernel<false, 256>;
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, reinterpret_cast<const uint16_t*>(H),
+                     (const int32_t*)nullptr, offsets, w_down, (const int8_t*)nullptr, scales, (void*)Y, d, f, E,
+                     rows_cap, order, splits_used);
   return hipGetLastError();
 }
 

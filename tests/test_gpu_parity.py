@@ -525,6 +525,30 @@ def test_kernel_paths_agree_across_a_boundary(T):
     assert np.max(np.abs(a - b[:T])) <= 1e-3 * rms(a)
 
 
+def test_tile_heights_agree_bitwise():
+    # Batches whose experts average at most 96 rows run the tiled kernels in 128-row tiles
+    # (tiles of at most 64 rows spread over all 8 wavefronts), larger ones in 256-row tiles.
+    # Every row gets the same MFMA sequence either way: 300 tokens with a biased router (one
+    # expert over two tiles, one tile at most 32 rows), then the same tokens plus 100 padded
+    # ones, which only raise the row capacity past the switch, must agree bit for bit.
+    T, dd, f = 300, 512, 1024
+    inp, d = small_case("tiles", T=T + 100, d=dd, f=f, n_pad=0, bias=(2.0, 1.0, 0.5, 0, 0, 0, 0, -1.0))
+    a, _ = run_forward(dict(d, x=d["x"][:T].contiguous()), T, dd, f, 8, 2)
+    pad = torch.ones(T + 100, dtype=torch.uint8, device="cuda")
+    pad[T:] = 0
+    b, _ = run_forward(dict(d, pad_mask=pad), T + 100, dd, f, 8, 2)
+    assert moe.down_splits(T, dd, f, 8, 2) == moe.down_splits(T + 100, dd, f, 8, 2) == 1
+    assert np.array_equal(a.view(np.uint32), b[:T].view(np.uint32))
+    assert np.all(b[T:] == 0)
+    ids = torch.empty((T, 2), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, 2), dtype=torch.float32, device="cuda")
+    moe.moe_route(d["x"], d["router_w"], d["router_bias"], None, ids, w, T, dd, 8, 2)
+    loads = np.bincount(ids.cpu().numpy().ravel(), minlength=8)
+    assert loads.max() > 128 and loads.min() <= 32, loads  # both tile kinds and an idle row tile
+    check_layer(dict(inp, x=np.ascontiguousarray(inp["x"][:T])), dict(d, x=d["x"][:T].contiguous()),
+                label="T=300 biased, 128-row tiles")
+
+
 def test_caller_workspace_matches_library_workspace():
     inp, d = small_case("ws", T=100, d=256, f=512, n_pad=5)
     a, _ = run_forward(d, 100, 256, 512, 8, 2)
