@@ -19,8 +19,9 @@
 //     operand is one 16-byte LDS read; column 2 c + q of a 64-column group goes to LDS
 //     row 32 q + c, which gives each lane 2 adjacent output columns in the epilogue.
 // Batches whose experts average at most 96 rows use 128-row tiles (half the activation
-// loads and LDS stores per slice; wavefronts 4-7 only move slices), and a tile of at most 64
-// rows spreads its 32x32 MFMA tiles over all 8 wavefronts so that all 4 SIMDs multiply.
+// loads and LDS stores per slice; wavefronts 4-7 only move slices); a tile of at most 64
+// rows gives its 32x32 MFMA tiles to wavefronts 0-3, one per SIMD, so that all 4 SIMDs
+// multiply, and moves only 64 activation rows per slice.
 // Rows are gathered through the dispatch permutation (gate/up) or read in segment order
 // (down). Tiles are assigned on the device: m-slots enumerate the m-tiles of all expert
 // segments in expert order (read from offsets), surplus slots exit at once; the order of
@@ -303,28 +304,36 @@ __global__ __launch_bounds__(kThreads) void expert_prefill_kernel(
   __syncthreads();
   if constexpr (kBM == 128) {
     if (rows <= 64) {  // uniform per workgroup
-      // Tiles of at most 64 rows: the same 32x32 MFMA tiles (so the same sums, bit for bit),
-      // spread over all 8 wavefronts instead of the 2 of row group 0, so that all 4 SIMDs
-      // multiply. Wavefront w takes row tile w / 4 and column pair c = w % 4:
-      //   gate/up: gate and up tiles at LDS rows (c / 2) * 64 + 32 (c % 2) (+ 128 for up),
-      //            i.e. column 2 (lane % 32) + c % 2 of 64-column group c / 2;
+      // Tiles of at most 64 rows: the same 32x32 MFMA tiles as below (so the same sums, bit
+      // for bit), taken by wavefronts 0-3, one per SIMD, instead of the two of row group 0;
+      // wavefronts 4-7 only move slices. Wavefront c (0-3) takes both 32-row tiles and
+      //   gate/up: the gate and up tiles at LDS rows (c / 2) * 64 + 32 (c % 2) (+ 128 for
+      //            up), i.e. column 2 (lane % 32) + c % 2 of 64-column group c / 2;
       //   down:    LDS rows (c / 2) * 128 + (c % 2) * 64 + 32 q (q = 0, 1), i.e. columns
       //            2 (lane % 32) + q of that group.
-      const int nm = wave >> 2, c = wave & 3;
+      // Each weight tile is read by one wavefront (by two when 8 wavefronts took 32 rows
+      // each: 1.5x the LDS reads, measured 4% slower), and only the first 64 activation rows
+      // are moved after the first slice.
+      const int c = wave & 3;
       int nbro[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         nbro[j] = (kGateUp ? j * HALF + (c >> 1) * 64 + 32 * (c & 1) : (c >> 1) * HALF + (c & 1) * 64 + 32 * j) +
                   (lane & 31);
-      const int narl = 32 * nm + (lane & 31);
-      f32x16 accn[2];
+      const int narl = lane & 31;
+      f32x16 accn[2][2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) accn[j][i] = 0.0f;
-      Frag na[2], nb[2][2];
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) accn[mt][j][i] = 0.0f;
+      Frag na[2][2], nb[2][2];
       auto read_n = [&](const uint16_t* st, int buf, int ks) {
-        na[buf] = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(st + (size_t)narl * LDS_LD + ks + kq));
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          na[buf][mt] =
+              __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(st + (size_t)(narl + 32 * mt) * LDS_LD + ks + kq));
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           nb[buf][j] =
@@ -336,29 +345,48 @@ __global__ __launch_bounds__(kThreads) void expert_prefill_kernel(
         for (int kk = 0; kk < BK / 16; ++kk) {
           if (kk + 1 < BK / 16) read_n(cur, (kk + 1) & 1, (kk + 1) * 16);
 #pragma unroll
-          for (int j = 0; j < 2; ++j) accn[j] = Mfma32<Frag>::run(na[kk & 1], nb[kk & 1][j], accn[j]);
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) accn[mt][j] = Mfma32<Frag>::run(na[kk & 1][mt], nb[kk & 1][j], accn[mt][j]);
         }
       };
-      if (__builtin_amdgcn_readfirstlane(nm * 32 < rows ? 1 : 0)) {  // uniform per wavefront
+      auto gload_n = [&](auto stage, int kk) {
+        constexpr int rs = decltype(stage)::value;
+        ra[rs][0] = *reinterpret_cast<const u32x4*>(arow[0] + kk);
+        const uint32_t sbase = (uint32_t)(kbeg + kk) * ldb;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) rb[rs][r] = __builtin_amdgcn_raw_buffer_load_b32(br, bvoff, sbase + r * ldb, 0);
+      };
+      auto store_n = [&](auto stage, uint16_t* st) {
+        constexpr int rs = decltype(stage)::value;
+        uint16_t* sB = st + A_ELEMS;
+        *reinterpret_cast<u32x4*>(st + (size_t)(tid / 8) * LDS_LD + 8 * (tid % 8)) = ra[rs][0];
+        store_col<kGateUp, 0>(sB, hb * HALF + brow + 0, 8 * kg, rb[rs]);
+        store_col<kGateUp, 1>(sB, hb * HALF + brow + 32, 8 * kg, rb[rs]);
+        store_col<kGateUp, 2>(sB, hb * HALF + brow + 1, 8 * kg, rb[rs]);
+        store_col<kGateUp, 3>(sB, hb * HALF + brow + 33, 8 * kg, rb[rs]);
+      };
+      if (__builtin_amdgcn_readfirstlane(wave < 4 ? 1 : 0)) {  // uniform per wavefront
         for (int it = 0; it < nslices; it += 2) {
-          gload(R0, min((it + 2) * BK, klast));
+          gload_n(R0, min((it + 2) * BK, klast));
           slice_n(L0);
-          lds_store(R1, L1);
+          store_n(R1, L1);
           __syncthreads();
-          gload(R1, min((it + 3) * BK, klast));
+          gload_n(R1, min((it + 3) * BK, klast));
           slice_n(L1);
-          lds_store(R0, L0);
+          store_n(R0, L0);
           __syncthreads();
         }
       } else {
         for (int it = 0; it < nslices; it += 2) {
-          gload(R0, min((it + 2) * BK, klast));
-          lds_store(R1, L1);
+          gload_n(R0, min((it + 2) * BK, klast));
+          store_n(R1, L1);
           __syncthreads();
-          gload(R1, min((it + 3) * BK, klast));
-          lds_store(R0, L0);
+          gload_n(R1, min((it + 3) * BK, klast));
+          store_n(R0, L0);
           __syncthreads();
         }
+        return;
       }
       const uint16_t* sc = scales + (size_t)e * (2 * (size_t)f + d);
       const int rq = 4 * (lane >> 5);
@@ -367,23 +395,28 @@ __global__ __launch_bounds__(kThreads) void expert_prefill_kernel(
         const float sg = bf16_bits_to_float(sc[n]), su = bf16_bits_to_float(sc[f + n]);
         _Float16* H = reinterpret_cast<_Float16*>(out);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int m = 32 * nm + 8 * (i >> 2) + rq + (i & 3);
-          if (m < rows) H[(size_t)(row0 + m) * f + n] = (_Float16)(gelu_tanh(accn[0][i] * sg) * (accn[1][i] * su));
-        }
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int m = 32 * mt + 8 * (i >> 2) + rq + (i & 3);
+            if (m < rows)
+              H[(size_t)(row0 + m) * f + n] = (_Float16)(gelu_tanh(accn[mt][0][i] * sg) * (accn[mt][1][i] * su));
+          }
       } else {
         float* Y = reinterpret_cast<float*>(out) + (size_t)blockIdx.z * rows_cap * d;
         const int n = n0 + (c >> 1) * HALF + (c & 1) * 64 + 2 * (lane & 31);
         const uint32_t s2 = *reinterpret_cast<const uint32_t*>(sc + 2 * (size_t)f + n);
         const float sd0 = bf16_bits_to_float(s2 & 0xFFFFu), sd1 = bf16_bits_to_float(s2 >> 16);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int m = 32 * nm + 8 * (i >> 2) + rq + (i & 3);
-          if (m < rows) {
-            u32x2 v = {__float_as_uint(accn[0][i] * sd0), __float_as_uint(accn[1][i] * sd1)};
-            *reinterpret_cast<u32x2*>(Y + (size_t)(row0 + m) * d + n) = v;
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int m = 32 * mt + 8 * (i >> 2) + rq + (i & 3);
+            if (m < rows) {
+              u32x2 v = {__float_as_uint(accn[mt][0][i] * sd0), __float_as_uint(accn[mt][1][i] * sd1)};
+              *reinterpret_cast<u32x2*>(Y + (size_t)(row0 + m) * d + n) = v;
+            }
           }
-        }
       }
       return;
     }
