@@ -276,10 +276,10 @@ def main() -> int:
                 "frac": round(gu_ach / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": rec["gate_up_traffic_bytes"] if rec else None,
                 "traffic_source": rec["profile"] if rec else None,
-                "kernel": "expert_prefill_kernel<true>", "algorithmic_flops_per_launch": work["gu_flops"],
+                "kernel": "expert_prefill_kernel<true, 256>", "algorithmic_flops_per_launch": work["gu_flops"],
                 "algorithmic_bytes_per_launch": work["gu_bytes_prefill"], "avg_launch_ms": round(gu_ms, 5)}
         layer_tf = work["layer_flops"] / (ms_per_step * 1e-3) / 1e12
-        kern = {"expert_prefill_kernel<false>": {"avg_launch_ms": round(dn_ms, 5), "achieved_TFLOPs": round(dn_ach, 1),
+        kern = {"expert_prefill_kernel<false, 256>": {"avg_launch_ms": round(dn_ms, 5), "achieved_TFLOPs": round(dn_ach, 1),
                                                  "frac": round(dn_ach / MFMA_BF16_PEAK_TFLOPS, 4)},
                 "layer": {"TFLOPs": round(layer_tf, 1), "mfma_frac": round(layer_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                           "algorithmic_flops": work["layer_flops"]}}

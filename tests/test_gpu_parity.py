@@ -549,6 +549,28 @@ def test_tile_heights_agree_bitwise():
                 label="T=300 biased, 128-row tiles")
 
 
+@pytest.mark.parametrize("T,n_pad", [(192, 0), (320, 11)])
+def test_layer_parity_grok_midsize(T, n_pad):
+    # Mid-size batches at the Grok shape run the tiled kernels in 128-row tiles: at 192 tokens
+    # the experts hold about 48 rows (narrow tiles), at 320 about 77 (65..128-row tiles)
+    host_w, dev_w = grok_weights()
+    spec = synth.replace(synth.CONFIGS["decode"], name="midsize", T=T, n_pad=n_pad, x_set=20 + T % 7)
+    inp = synth.make_inputs(spec, with_weights=False)
+    inp.update({n: host_w[n] for n in ("w_gate", "w_up", "w_down")})
+    inp["k"] = 2
+    d = to_dev(inp, with_weights=False)
+    d.update({n: dev_w[n] for n in ("w_gate", "w_up", "w_down")})
+    pads = None if inp["pad_mask"] is None else np.nonzero(inp["pad_mask"] == 0)[0][:1]
+    rows = sample_rows(T, 8, seed=T, must=pads)
+    _, dbg, _ = check_layer(inp, d, rows=rows, label=f"grok T={T}")
+    counts = dbg["counts"]
+    print(f"[grok T={T}] rows per expert {counts.tolist()}", flush=True)
+    if T == 192:
+        assert counts.min() <= 64
+    else:
+        assert np.any((counts > 64) & (counts <= 128))
+
+
 def test_caller_workspace_matches_library_workspace():
     inp, d = small_case("ws", T=100, d=256, f=512, n_pad=5)
     a, _ = run_forward(d, 100, 256, 512, 8, 2)
