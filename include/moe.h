@@ -137,8 +137,9 @@ int moe_gate_up(const void* x, const int32_t* perm, const int32_t* offsets, cons
    with the contraction over f cut into `splits` equal parts: y fp32 [splits][T*k][d] holds
    one partial sum per part (their sum, in part order, is the result). splits must divide
    f / 128. moe_down_splits() gives the count moe_forward launches with for a shape; at
-   T > 160 moe_forward's own down launch may then keep 1 of those 2 parts, which its combine
-   learns on the device (this entry point always writes exactly `splits`). */
+   T > 160 moe_forward's own down launch may then keep fewer of those 2 or 4 parts (1 or 2;
+   1, 2 or 4), which its combine learns on the device (this entry point always writes exactly
+   `splits`). */
 int moe_down(const void* h, const int32_t* offsets, const int8_t* w_down, const void* scales,
              float* y, int splits, int T, int d, int f, int E, int k, void* stream);
 int moe_down_splits(int T, int d, int f, int E, int k);

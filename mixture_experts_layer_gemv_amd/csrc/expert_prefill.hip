@@ -137,17 +137,27 @@ __device__ __forceinline__ void tile_of(int w, const TileOrder& o, int& mslot, i
   ntile = xj * nblk + g * o.ngroup + rem % o.ngroup;
 }
 
-// Parts of the down contraction when the kernel may choose 1 or 2: the live workgroups run in
-// rounds of ncu (one per CU); two parts fill a ragged last round better but cost a second fp32
-// partial, 8 bytes per output element (written, then read by the combine) at about 5 TB/s
-// against 2 f FLOPs at about 1 PFLOP/s, i.e. about 800 / f of the kernel's time.
-__device__ __forceinline__ int down_parts(const int32_t* offsets, int E, int bm, int ntiles, int ncu, int f) {
+// Parts of the down contraction when the kernel may choose 1, 2 or 4 (at most maxp): the live
+// workgroups run in rounds of ncu (one per CU), so p parts take ceil(p r) / p full-length
+// rounds for r = live tiles / ncu; more parts fill a ragged last round better, but each extra
+// one costs an fp32 partial, 8 bytes per output element (written, then read by the combine)
+// at about 5 TB/s against 2 f FLOPs at about 1 PFLOP/s, i.e. about 800 / f of the kernel's time.
+// Four parts only while one part cannot fill a round (r <= 1): beyond that the model overrates
+// quarter-length workgroups (measured at 1024 tokens: 4 parts 0.6% slower than the 2 it kept).
+__device__ __forceinline__ int down_parts(const int32_t* offsets, int E, int bm, int ntiles, int ncu, int f,
+                                          int maxp) {
   int live = 0;
   for (int e = 0; e < E; ++e) live += (offsets[e + 1] - offsets[e] + bm - 1) / bm;
   if (live == 0) return 1;
-  const float r1 = (float)(live * ntiles) / (float)ncu, r2 = 2.0f * r1;
-  const float fill1 = ceilf(r1) / r1, fill2 = ceilf(r2) / r2;
-  return fill1 > fill2 + 800.0f / (float)f ? 2 : 1;
+  const float r1 = (float)(live * ntiles) / (float)ncu;
+  int best = 1;
+  float bt = ceilf(r1) / r1;
+  for (int p = 2; p <= maxp && (p == 2 || r1 <= 1.0f); p *= 2) {
+    const float rp = (float)p * r1;
+    const float t = ceilf(rp) / rp + (float)(p - 1) * 800.0f / (float)f;
+    if (t < bt) best = p, bt = t;
+  }
+  return best;
 }
 
 // kBM: rows per tile, 256 or 128.
@@ -161,8 +171,8 @@ __global__ __launch_bounds__(kThreads) void expert_prefill_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE_ELEMS];
 
   int parts = gridDim.z;
-  if (!kGateUp && splits_used != nullptr) {  // launched with 2 parts: keep 1 or 2
-    parts = down_parts(offsets, E, kBM, order.ntiles, order.ncu, f);
+  if (!kGateUp && splits_used != nullptr) {  // launched with 2 or 4 parts: keep 1, 2 or 4
+    parts = down_parts(offsets, E, kBM, order.ntiles, order.ncu, f, (int)gridDim.z);
     if (blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x == 0) *splits_used = parts;
     if ((int)blockIdx.z >= parts) return;
   }
@@ -540,7 +550,7 @@ hipError_t launch_gate_up_prefill(const uint16_t* x, const int32_t* perm, const 
 hipError_t launch_down_prefill(const _Float16* H, const int32_t* offsets, const int8_t* w_down,
                                const uint16_t* scales, float* Y, int splits, int rows_cap, int d,
                                int f, int E, int* splits_used, hipStream_t stream) {
-  if (splits_used != nullptr && splits != 2) return hipErrorInvalidValue;
+  if (splits_used != nullptr && splits != 2 && splits != 4) return hipErrorInvalidValue;
   const int bm = prefill_bm(rows_cap, E);
   const int nslots = prefill_mslots(rows_cap, E, bm), ntiles = d / (2 * HALF);
   // every XCD takes its own weight columns, as for gate/up (measured against 2 x 4 and 4 x 2

@@ -16,12 +16,19 @@ namespace moe {
 // each wavefront carries one 16-row tile (T <= 16) and about 512 with two (longer streams win
 // once the MFMA work per byte doubles), with parts of at least 1024 rows (shorter ones lose
 // to their start-up). At most 8 parts, each a whole number of 128-row steps.
-// Large batches: the most parts the prefill down kernel may use. Launched with 2, it keeps
-// 1 or 2 on the device (from the live tile count, which only the device knows) and reports
-// the choice to the combine.
+// Large batches: the most parts the prefill down kernel may use. Launched with 2 or 4, it
+// keeps 1, 2 or 4 on the device (from the live tile count, which only the device knows) and
+// reports the choice to the combine. 4 where one part is expected to fill less than a round
+// of 256 workgroups (about T * k / 256 + E / 2 row tiles x d / 256 column tiles; the kernel
+// only takes 4 then) and the fp32 partials stay modest (T * k <= 8192 rows).
 // The slab counts take the experts a batch can touch, min(E, T * k): at T = 1 only two stream.
 inline int down_splits(int T, int d, int f, int E, int k) {
-  if (T > kDecodeMaxT) return f >= 8192 ? 2 : 1;
+  if (T > kDecodeMaxT) {
+    if (f < 8192) return 1;
+    const long rows = (long)T * k;
+    const long tiles = (rows + 255) / 256 + std::min<long>(E, rows) / 2;
+    return rows <= 8192 && tiles * (d / 256) <= 256 && (f / 128) % 4 == 0 ? 4 : 2;
+  }
   const long slabs = (long)(d / 256) * std::min<long>(E, (long)T * k);
   const long target = T <= 16 ? 1024 : 512;
   int s = 1;

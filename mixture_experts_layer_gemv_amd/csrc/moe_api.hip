@@ -94,8 +94,8 @@ Layout make_layout(int T, int d, int f, int E, int k) {
   L.dchunk = nchunks > 0 ? take((size_t)2 * nchunks * E * 4) : 0;
   const size_t rp_floats = moe::router_partial_floats(T, d, E);
   L.rp = rp_floats > 0 ? take(rp_floats * 4) : 0;
-  // large batches: the number of down parts the prefill kernel kept (it may keep 1 of 2)
-  L.sused = (T > moe::kDecodeMaxT && L.splits == 2) ? take(4) : 0;
+  // large batches: the number of down parts the prefill kernel kept (of the 2 or 4 launched)
+  L.sused = (T > moe::kDecodeMaxT && L.splits >= 2) ? take(4) : 0;
   L.total = at;
   return L;
 }

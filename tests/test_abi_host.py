@@ -98,9 +98,17 @@ def test_workspace_size_and_split_policy():
     # the policy counts the experts a batch can reach, min(E, T * k)
     assert moe.down_splits(1, 6144, 4096, 8, 2) == 4
     assert moe.workspace_bytes(1, 6144, 4096, 8, 2) >= 2 * 8 * 2 * 4096 * 4  # 8 gate/up parts
-    # prefill, long contraction: launched with 2 parts, of which the kernel keeps 1 or 2
+    # prefill, long contraction: launched with 2 or 4 parts, of which the kernel keeps fewer or all
     assert moe.down_splits(8192, 6144, 32768, 8, 2) == 2
-    assert moe.down_splits(161, 256, 8192, 8, 2) == 2
+    # 4 where one part is expected to under-fill a round of 256 workgroups (about
+    # T * k / 256 + E / 2 row tiles x d / 256 column tiles) and T * k <= 8192
+    assert moe.down_splits(161, 256, 8192, 8, 2) == 4
+    assert moe.down_splits(768, 6144, 32768, 8, 2) == 4  # 10 x 24 tiles
+    assert moe.down_splits(1024, 6144, 32768, 8, 2) == 2  # 12 x 24
+    assert moe.down_splits(4096, 256, 8192, 8, 2) == 4
+    assert moe.down_splits(4097, 256, 8192, 8, 2) == 2
+    assert moe.down_splits(200, 256, 8448, 8, 2) == 2  # f / 128 = 66: quarters are not whole 128-row steps
+    assert moe.down_splits(200, 256, 4096, 8, 2) == 1
     # up to 160 tokens the streaming kernels run, with the small-batch policy
     assert moe.down_splits(160, 256, 8192, 8, 2) == 8
     # the gate/up split's partial sums are part of the decode workspace at narrow f
