@@ -386,6 +386,10 @@ def small_case(name, **kw):
     # and with a biased router that sends one expert over 48 rows (several passes)
     dict(T=100, d=6144, f=1024, E=8, k=2, n_pad=6),
     dict(T=160, d=256, f=512, E=8, k=2, bias=(3.0, 2.0, 0, 0, 0, 0, 0, 0)),
+    # above 160 tokens with many experts: 128-row tiles, most of them narrow (16 experts x
+    # about 50 rows; 64 experts x about 9 rows, many tiles idle in their second 32 rows)
+    dict(T=200, d=256, f=768, E=16, k=4, n_pad=7),
+    dict(T=300, d=512, f=512, E=64, k=2),
 ])
 def test_layer_edge_shapes(kw):
     inp, d = small_case("edge", **kw)
