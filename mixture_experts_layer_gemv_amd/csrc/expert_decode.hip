@@ -361,7 +361,7 @@ hipError_t launch_down_decode(const _Float16* H, const int32_t* offsets, const i
                               int d, int f, int E, hipStream_t stream) {
   dim3 grid(d / kSlab, splits, E), block(64);
   if (T <= 16)
-    hipLaunchKernelGGL((down_decode_kernel<1, 3>), grid, block, 0, stream, H, offsets, w_down, scales, Y, d,
+    hipLaunchKernelGGL((down_decode_kernel<1, 4>), grid, block, 0, stream, H, offsets, w_down, scales, Y, d,
                        f, rows_cap);
   else if (T <= 64)
     hipLaunchKernelGGL((down_decode_kernel<2, 4>), grid, block, 0, stream, H, offsets, w_down, scales, Y, d,

@@ -12,8 +12,9 @@
 namespace moe {
 
 // Small batches (T <= 64), targets measured on whole forward passes at the Grok-1 shape and
-// at one GPU's tensor-parallel share: the down projection wants about 1024 workgroups while
-// each wavefront carries one 16-row tile (T <= 16) and about 512 with two (longer streams win
+// at one GPU's tensor-parallel share: the down projection wants about 768 workgroups while
+// each wavefront carries one 16-row tile (T <= 16: one wavefront per SIMD with a 4-step load
+// ring, so that all of them are resident at once) and about 512 with two (longer streams win
 // once the MFMA work per byte doubles), with parts of at least 1024 rows (shorter ones lose
 // to their start-up). At most 8 parts, each a whole number of 128-row steps.
 // Large batches: the most parts the prefill down kernel may use. Launched with 2 or 4, it
@@ -30,7 +31,7 @@ inline int down_splits(int T, int d, int f, int E, int k) {
     return rows <= 8192 && tiles * (d / 256) <= 256 && (f / 128) % 4 == 0 ? 4 : 2;
   }
   const long slabs = (long)(d / 256) * std::min<long>(E, (long)T * k);
-  const long target = T <= 16 ? 1024 : 512;
+  const long target = T <= 16 ? 768 : 512;
   int s = 1;
   while (s < 8 && slabs * s < target && f / (2 * s) >= 1024 && (f / 128) % (2 * s) == 0) s *= 2;
   return s;
