@@ -9,7 +9,8 @@
 // alone are too few to fill the chip (narrow f, e.g. one GPU's share of a tensor-parallel
 // split). For gate/up a workgroup holds two wavefronts, one per matrix, on the same slab;
 // they meet in LDS for the GeGLU epilogue, or, when the contraction is split, write fp32
-// partial sums that geglu_finish_kernel adds in part order before the same epilogue. Lane l takes the 16 adjacent columns
+// partial sums that geglu_finish_kernel adds in part order before the same epilogue; at
+// T <= 4 one wavefront streams both matrices (gate_up_fused_decode_kernel). Lane l takes the 16 adjacent columns
 // n0 + 16 (l % 16) .. + 15 and, per 32-deep step, the rows k0 + 8 (l / 16) .. + 7: eight
 // 16-byte loads, so each row segment a wavefront instruction touches is 256 contiguous
 // bytes. Byte j of those eight rows is exactly the B operand of one 16x16x32 MFMA (column
@@ -101,6 +102,64 @@ __device__ __forceinline__ void stream_slab(__amdgpu_buffer_rsrc_t wr, uint32_t 
     MOE_DEC_COL(8) MOE_DEC_COL(9) MOE_DEC_COL(10) MOE_DEC_COL(11)
     MOE_DEC_COL(12) MOE_DEC_COL(13) MOE_DEC_COL(14) MOE_DEC_COL(15)
 #undef MOE_DEC_COL
+  };
+
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < steps) load(s, s);
+  int st = 0;
+  for (; st + 2 * kStages - 1 <= steps; st += kStages) {
+#pragma unroll
+    for (int s = 0; s < kStages; ++s) {
+      load((s + kStages - 1) % kStages, st + s + kStages - 1);
+      compute(s);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < 2 * kStages - 1; ++s) {
+    if (st + s < steps) {
+      if (st + s + kStages - 1 < steps) load((s + kStages - 1) % kStages, st + s + kStages - 1);
+      compute(s % kStages);
+    }
+  }
+}
+
+// The same stream over two matrices at once (gate and up of one slab): both rings share
+// the activation loads; accg / accu take the two products.
+template <typename Frag, int MT, int kStages>
+__device__ __forceinline__ void stream_slab2(__amdgpu_buffer_rsrc_t wg, __amdgpu_buffer_rsrc_t wu, uint32_t voff,
+                                             uint32_t ld, int steps, const uint16_t* const (&a)[MT],
+                                             f32x4 (&accg)[MT][kNcol], f32x4 (&accu)[MT][kNcol]) {
+  constexpr int NW = kNcol / 4;
+  uint32_t bg[kStages][8][NW], bu[kStages][8][NW];
+  u32x4 av[kStages][MT];
+  auto load = [&](int s, int step) {
+    const uint32_t base = (uint32_t)step * kStep * ld;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) load_row<NW>(bg[s][r], wg, voff, base + r * ld);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) load_row<NW>(bu[s][r], wu, voff, base + r * ld);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) av[s][mt] = load16(a[mt] + step * kStep);
+  };
+  auto compute = [&](int s) {
+    Frag af[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) af[mt] = __builtin_bit_cast(Frag, av[s][mt]);
+#define MOE_DEC_COL2(J)                                                         \
+  if constexpr ((J) < kNcol) {                                                  \
+    Frag bfg = col_operand<(J), Frag, NW>(bg[s]);                               \
+    Frag bfu = col_operand<(J), Frag, NW>(bu[s]);                               \
+    _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) {                         \
+      accg[mt][(J)] = Mfma<Frag>::run(af[mt], bfg, accg[mt][(J)]);              \
+      accu[mt][(J)] = Mfma<Frag>::run(af[mt], bfu, accu[mt][(J)]);              \
+    }                                                                           \
+  }
+    MOE_DEC_COL2(0) MOE_DEC_COL2(1) MOE_DEC_COL2(2) MOE_DEC_COL2(3)
+    MOE_DEC_COL2(4) MOE_DEC_COL2(5) MOE_DEC_COL2(6) MOE_DEC_COL2(7)
+    MOE_DEC_COL2(8) MOE_DEC_COL2(9) MOE_DEC_COL2(10) MOE_DEC_COL2(11)
+    MOE_DEC_COL2(12) MOE_DEC_COL2(13) MOE_DEC_COL2(14) MOE_DEC_COL2(15)
+#undef MOE_DEC_COL2
   };
 
 #pragma unroll
@@ -232,6 +291,64 @@ __global__ __launch_bounds__(128) void gate_up_decode_kernel(
   }
 }
 
+// gate/up + GeGLU for T <= 4 (whole contraction): one wavefront per slab streams both
+// matrices with a 2-step ring each, sharing the activation loads, and applies the GeGLU in
+// registers (no LDS exchange). Same MFMA sequence per output as gate_up_decode_kernel, so the
+// same bits. With 2-5 touched experts the two-wavefront form runs 1.3-1.5 rounds of
+// wavefronts where this one runs under one (T = 3: 565 -> 487 us per forward at the Grok
+// shape); from T = 5 the deeper single-matrix rings win.
+// grid (f / kSlab, 1, E), block 64.
+template <int MT, int kStages>
+__global__ __launch_bounds__(64) void gate_up_fused_decode_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
+    const int8_t* __restrict__ w_gate, const int8_t* __restrict__ w_up, const uint16_t* __restrict__ scales,
+    _Float16* __restrict__ H, int d, int f) {
+  const int e = blockIdx.z;
+  const int row0 = offsets[e];
+  const int M = offsets[e + 1] - row0;
+  if (M <= 0) return;
+  const int lane = threadIdx.x, kg = lane >> 4, cl = lane & 15;
+  const int n0 = blockIdx.x * kSlab + kNcol * cl;
+  const __amdgpu_buffer_rsrc_t wg = weight_rsrc(w_gate + (size_t)e * d * f, (size_t)d * f);
+  const __amdgpu_buffer_rsrc_t wu = weight_rsrc(w_up + (size_t)e * d * f, (size_t)d * f);
+  const uint32_t voff = (uint32_t)(8 * kg) * (uint32_t)f + (uint32_t)n0;
+  for (int pb = 0; pb < M; pb += 16 * MT) {
+    const uint16_t* a[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = min(pb + 16 * mt + cl, M - 1);
+      a[mt] = x + (size_t)perm[row0 + m] * d + 8 * kg;
+    }
+    f32x4 accg[MT][kNcol], accu[MT][kNcol];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < kNcol; ++j) accg[mt][j] = accu[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    stream_slab2<bf16x8, MT, kStages>(wg, wu, voff, (uint32_t)f, d / kStep, a, accg, accu);
+    float sg[kNcol], su[kNcol];
+    load_scales<kNcol>(scales + (size_t)e * (2 * (size_t)f + d) + n0, sg);
+    load_scales<kNcol>(scales + (size_t)e * (2 * (size_t)f + d) + f + n0, su);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = pb + 16 * mt + 4 * kg + i;
+        if (m < M) {
+#pragma unroll
+          for (int q = 0; q < kNcol / 8; ++q) {
+            uint32_t packed[4];
+#pragma unroll
+            for (int j = 8 * q; j < 8 * q + 8; j += 2)
+              packed[(j >> 1) & 3] = pack_f16_rne(gelu_tanh(accg[mt][j][i] * sg[j]) * (accu[mt][j][i] * su[j]),
+                                                  gelu_tanh(accg[mt][j + 1][i] * sg[j + 1]) * (accu[mt][j + 1][i] * su[j + 1]));
+            u32x4 v = {packed[0], packed[1], packed[2], packed[3]};
+            *reinterpret_cast<u32x4*>(H + (size_t)(row0 + m) * f + n0 + 8 * q) = v;
+          }
+        }
+      }
+  }
+}
+
 // ------------------------------------------------------------------------------------
 // The GeGLU epilogue of a split gate/up contraction: for row r < offsets[E] (expert e),
 // g = s_g * (sum over parts p in order of P[2p][r]), u likewise from P[2p + 1]; H[r] =
@@ -343,6 +460,9 @@ hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* perm, const i
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(geglu_finish_kernel, dim3(rows_cap, (f + 2047) / 2048), dim3(256), 0, stream, P, offsets,
                        scales, H, parts, d, f, E, rows_cap);
+  } else if (T <= 4) {
+    hipLaunchKernelGGL((gate_up_fused_decode_kernel<1, 2>), dim3(f / kSlab, 1, E), dim3(64), 0, stream, x, perm,
+                       offsets, w_gate, w_up, scales, H, d, f);
   } else if (T <= 16) {
     hipLaunchKernelGGL((gate_up_decode_kernel<1, 4, false>), grid, block, 0, stream, x, perm, offsets, w_gate,
                        w_up, scales, H, P, d, f, rows_cap);
