@@ -97,6 +97,7 @@ def test_workspace_size_and_split_policy():
     assert moe.down_splits(8192, 6144, 4096, 8, 2) == 1
     # the policy counts the experts a batch can reach, min(E, T * k)
     assert moe.down_splits(1, 6144, 4096, 8, 2) == 4
+    assert moe.down_splits(1, 6144, 32768, 8, 2) == 16  # two experts x 24 slabs: 16 parts fill the chip
     assert moe.workspace_bytes(1, 6144, 4096, 8, 2) >= 2 * 8 * 2 * 4096 * 4  # 8 gate/up parts
     # prefill, long contraction: launched with 2 or 4 parts, of which the kernel keeps fewer or all
     assert moe.down_splits(8192, 6144, 32768, 8, 2) == 2

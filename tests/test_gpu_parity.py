@@ -390,6 +390,10 @@ def small_case(name, **kw):
     # about 50 rows; 64 experts x about 9 rows, many tiles idle in their second 32 rows)
     dict(T=200, d=256, f=768, E=16, k=4, n_pad=7),
     dict(T=300, d=512, f=512, E=64, k=2),
+    # few slabs and a long contraction over f: the down projection in 16 parts (T = 1 and T = 3,
+    # the latter with one gate/up wavefront streaming both matrices)
+    dict(T=1, d=256, f=16384),
+    dict(T=3, d=256, f=16384, scale_jitter=True),
 ])
 def test_layer_edge_shapes(kw):
     inp, d = small_case("edge", **kw)
