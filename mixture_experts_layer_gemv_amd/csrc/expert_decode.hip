@@ -21,8 +21,9 @@
 // after the contraction. Loads run kStages - 1 steps ahead of the MFMAs (register ring).
 //
 // Rows: an expert's segment of the dispatch has M rows (M <= T). A pass covers MT
-// 16-row MFMA tiles (MT = 1 when T <= 16, 2 when T <= 64, else 3, the most the registers
-// hold); longer segments take further passes over the weights.
+// 16-row MFMA tiles (MT = 1 when T <= 16 (gate/up with the whole contraction: T <= 8), 2
+// when T <= 64, else 3, the most the registers hold); longer segments take further passes
+// over the weights.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -463,7 +464,7 @@ hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* perm, const i
   } else if (T <= 4) {
     hipLaunchKernelGGL((gate_up_fused_decode_kernel<1, 2>), dim3(f / kSlab, 1, E), dim3(64), 0, stream, x, perm,
                        offsets, w_gate, w_up, scales, H, d, f);
-  } else if (T <= 16) {
+  } else if (T <= 8) {  // 9-16 tokens: the 32-row passes below were as fast or faster (T = 16: -1.8%)
     hipLaunchKernelGGL((gate_up_decode_kernel<1, 4, false>), grid, block, 0, stream, x, perm, offsets, w_gate,
                        w_up, scales, H, P, d, f, rows_cap);
   } else if (T <= 64) {

@@ -522,13 +522,13 @@ def test_doubling_down_scales_doubles_out_exactly(T):
     assert np.max(np.abs(b - 2 * a)) <= 1e-3 * rms(2 * a)
 
 
-@pytest.mark.parametrize("T", [4, 16, 64, 160])
+@pytest.mark.parametrize("T", [4, 8, 16, 64, 160])
 def test_kernel_paths_agree_across_a_boundary(T):
     # T tokens, then the same tokens plus one padded token. At 4 | 5 gate/up goes from one
-    # wavefront streaming both matrices to one per matrix, at 16 | 17 and 64 | 65 the
-    # streaming kernels go from 16- to 32- and from 32- to 48-row passes (each row's MFMA
-    # sequence is unchanged: the same bits); at 160 | 161 the tiled kernels take over (the
-    # real rows agree to the output tolerance)
+    # wavefront streaming both matrices to one per matrix, at 8 | 9 (gate/up) and 16 | 17
+    # (down) the streaming kernels go from 16- to 32-row passes and at 64 | 65 from 32- to
+    # 48-row passes (each row's MFMA sequence is unchanged: the same bits); at 160 | 161 the
+    # tiled kernels take over (the real rows agree to the output tolerance)
     inp, d = small_case("paths", T=T + 1, d=512, f=768, n_pad=0)
     a, _ = run_forward(dict(d, x=d["x"][:T].contiguous()), T, 512, 768, 8, 2)
     pad = torch.ones(T + 1, dtype=torch.uint8, device="cuda")
