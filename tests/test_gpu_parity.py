@@ -564,10 +564,12 @@ def test_tile_heights_agree_bitwise():
                 label="T=300 biased, 128-row tiles")
 
 
-@pytest.mark.parametrize("T,n_pad", [(192, 0), (320, 11)])
+@pytest.mark.parametrize("T,n_pad", [(1, 0), (3, 0), (192, 0), (320, 11)])
 def test_layer_parity_grok_midsize(T, n_pad):
-    # Mid-size batches at the Grok shape run the tiled kernels in 128-row tiles: at 192 tokens
-    # the experts hold about 48 rows (narrow tiles), at 320 about 77 (65..128-row tiles)
+    # Other batch sizes at the Grok shape: one token (two experts, the down projection in 16
+    # parts), three (one gate/up wavefront per slab streaming both matrices), and mid-size
+    # batches in the tiled kernels' 128-row tiles: at 192 tokens the experts hold about 48
+    # rows (narrow tiles), at 320 about 77 (65..128-row tiles)
     host_w, dev_w = grok_weights()
     spec = synth.replace(synth.CONFIGS["decode"], name="midsize", T=T, n_pad=n_pad, x_set=20 + T % 7)
     inp = synth.make_inputs(spec, with_weights=False)
@@ -580,8 +582,10 @@ def test_layer_parity_grok_midsize(T, n_pad):
     _, dbg, _ = check_layer(inp, d, rows=rows, label=f"grok T={T}")
     counts = dbg["counts"]
     print(f"[grok T={T}] rows per expert {counts.tolist()}", flush=True)
-    if T == 192:
-        assert counts.min() <= 64
+    if T <= 3:
+        assert moe.down_splits(T, 6144, 32768, 8, 2) == (16 if T == 1 else 8)
+    elif T == 192:
+        assert counts.max() <= 64
     else:
         assert np.any((counts > 64) & (counts <= 128))
 
