@@ -183,6 +183,22 @@ __device__ __forceinline__ void stream_slab2(__amdgpu_buffer_rsrc_t wg, __amdgpu
   }
 }
 
+// Rows of the largest expert segment (E <= 64 reads of offsets, the same for every workgroup).
+__device__ __forceinline__ int max_segment(const int32_t* __restrict__ offsets, int E) {
+  int m = 0;
+  for (int e = 0; e < E; ++e) m = max(m, offsets[e + 1] - offsets[e]);
+  return m;
+}
+
+// kOnly: 0 = always run; 1 = run only if no expert segment exceeds 32 rows; 2 = only if one
+// does (the 32- and 48-row kernels launched back to back, one of them leaving at once).
+template <int kOnly>
+__device__ __forceinline__ bool skip_by_segment(const int32_t* __restrict__ offsets, int E) {
+  if constexpr (kOnly == 0) return false;
+  const int m = max_segment(offsets, E);
+  return kOnly == 1 ? m > 32 : m <= 32;
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const int8_t* base, size_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(base), (short)0, (int)bytes, kBufferFlags);
 }
@@ -203,13 +219,14 @@ __device__ __forceinline__ void load_scales(const uint16_t* p, float (&s)[N]) {
 // grid (f / kSlab, parts, E), block 128: wavefront 0 = gate, wavefront 1 = up.
 // kPartial (parts > 1): part p of the contraction writes its unscaled sums to
 // P[(2 p + matrix) * rows_cap + row][n] (fp32) instead; geglu_finish_kernel completes H.
-template <int MT, int kStages, bool kPartial>
+template <int MT, int kStages, bool kPartial, int kOnly = 0>
 __global__ __launch_bounds__(128) void gate_up_decode_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, const int8_t* __restrict__ w_gate,
     const int8_t* __restrict__ w_up, const uint16_t* __restrict__ scales, _Float16* __restrict__ H,
     float* __restrict__ P, int d, int f, int rows_cap) {
   __shared__ float s_up[kPartial ? 1 : MT * 16][kSlab + 4];  // s_u * U of the pass, [row][slab column]
+  if (skip_by_segment<kOnly>(offsets, gridDim.z)) return;
   const int e = blockIdx.z, part = blockIdx.y;
   const int row0 = offsets[e];
   const int M = offsets[e + 1] - row0;
@@ -390,11 +407,12 @@ __global__ __launch_bounds__(256) void geglu_finish_kernel(const float* __restri
 // ------------------------------------------------------------------------------------
 // down: Y[s][row0 + m][n] = s_d[n] * sum over k in part s of H[row0 + m][k] * q_d[k][n]
 // grid (d / kSlab, splits, E), block 64.
-template <int MT, int kStages>
+template <int MT, int kStages, int kOnly = 0>
 __global__ __launch_bounds__(64) void down_decode_kernel(
     const _Float16* __restrict__ H, const int32_t* __restrict__ offsets,
     const int8_t* __restrict__ w_down, const uint16_t* __restrict__ scales, float* __restrict__ Y,
     int d, int f, int rows_cap) {
+  if (skip_by_segment<kOnly>(offsets, gridDim.z)) return;
   const int e = blockIdx.z, part = blockIdx.y;
   const int row0 = offsets[e];
   const int M = offsets[e + 1] - row0;
@@ -470,6 +488,13 @@ hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* perm, const i
   } else if (T <= 64) {
     hipLaunchKernelGGL((gate_up_decode_kernel<2, 3, false>), grid, block, 0, stream, x, perm, offsets, w_gate,
                        w_up, scales, H, P, d, f, rows_cap);
+  } else if (T <= 96) {
+    // 65-96 tokens: the 32-row passes stream 2% faster while no expert exceeds 32 rows, which
+    // only the device knows; both kernels are launched and one of them leaves at once
+    hipLaunchKernelGGL((gate_up_decode_kernel<2, 3, false, 1>), grid, block, 0, stream, x, perm, offsets, w_gate,
+                       w_up, scales, H, P, d, f, rows_cap);
+    hipLaunchKernelGGL((gate_up_decode_kernel<3, 3, false, 2>), grid, block, 0, stream, x, perm, offsets, w_gate,
+                       w_up, scales, H, P, d, f, rows_cap);
   } else {
     hipLaunchKernelGGL((gate_up_decode_kernel<3, 3, false>), grid, block, 0, stream, x, perm, offsets, w_gate,
                        w_up, scales, H, P, d, f, rows_cap);
@@ -487,7 +512,12 @@ hipError_t launch_down_decode(const _Float16* H, const int32_t* offsets, const i
   else if (T <= 64)
     hipLaunchKernelGGL((down_decode_kernel<2, 4>), grid, block, 0, stream, H, offsets, w_down, scales, Y, d,
                        f, rows_cap);
-  else
+  else if (T <= 96) {  // as for gate/up: 32-row passes unless an expert exceeds 32 rows
+    hipLaunchKernelGGL((down_decode_kernel<2, 4, 1>), grid, block, 0, stream, H, offsets, w_down, scales, Y, d,
+                       f, rows_cap);
+    hipLaunchKernelGGL((down_decode_kernel<3, 3, 2>), grid, block, 0, stream, H, offsets, w_down, scales, Y, d,
+                       f, rows_cap);
+  } else
     hipLaunchKernelGGL((down_decode_kernel<3, 3>), grid, block, 0, stream, H, offsets, w_down, scales, Y, d,
                        f, rows_cap);
   return hipGetLastError();

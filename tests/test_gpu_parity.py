@@ -386,6 +386,11 @@ def small_case(name, **kw):
     # and with a biased router that sends one expert over 48 rows (several passes)
     dict(T=100, d=6144, f=1024, E=8, k=2, n_pad=6),
     dict(T=160, d=256, f=512, E=8, k=2, bias=(3.0, 2.0, 0, 0, 0, 0, 0, 0)),
+    # 65..96 tokens: the 32-row kernels run unless an expert exceeds 32 rows (the 65-token cases
+    # above), then the 48-row ones (a biased router sends 76 of 78 tokens to expert 0; 96
+    # unbiased tokens give one expert 34 rows)
+    dict(T=80, d=256, f=512, E=8, k=2, bias=(3.0, 2.0, 0, 0, 0, 0, 0, 0), n_pad=2),
+    dict(T=96, d=512, f=768, E=8, k=2, n_pad=3),
     # above 160 tokens with many experts: 128-row tiles, most of them narrow (16 experts x
     # about 50 rows; 64 experts x about 9 rows, many tiles idle in their second 32 rows)
     dict(T=200, d=256, f=768, E=16, k=4, n_pad=7),
