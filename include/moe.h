@@ -126,7 +126,8 @@ int moe_dispatch(const int32_t* topk_ids, const uint8_t* pad_mask, int32_t* coun
    segment take x[perm[r]]; g, u = that row times the dequantised gate / up matrices
    (fp32 accumulation, per-output-channel scales applied in fp32); h = gelu_tanh(g) * u,
    stored as fp16 in h [T*k][f] at row r. Rows at or beyond offsets[E] are not written.
-   At T <= 160 with narrow f (too few 256-column slabs to fill the chip) the contraction over
+   At T <= 160 with narrow f (too few 256-column slabs to fill the chip; expert matrices above
+   2^23 weights, which take the streaming kernels there) the contraction over
    d is split as in moe_forward; the partial sums then live in the library workspace, which
    this call may allocate (MOE_ERR_NOMEM if it cannot) and which overlapping calls share. */
 int moe_gate_up(const void* x, const int32_t* perm, const int32_t* offsets, const int8_t* w_gate,

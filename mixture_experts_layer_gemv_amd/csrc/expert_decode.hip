@@ -1,7 +1,8 @@
-// Expert FFN for small batches (T <= 64): the layer streams the int8 weights of the
-// experts it touches once from HBM, so these kernels are built for bytes in flight,
-// not for reuse. (Grok-1 Admin & Architecture Guide, section 3, MoE step 3: the gated
-// GeLU expert gelu(linear(x)) * linear_v(x) -> linear_1; "Quantized weights": int8
+// Expert FFN for small batches (T <= 160, expert matrices above 2^23 weights): the
+// layer streams the int8 weights of the experts it touches once from HBM, so these
+// kernels are built for bytes in flight, not for reuse. (Grok-1 Admin & Architecture
+// Guide, section 3, MoE step 3: the gated GeLU expert gelu(linear(x)) * linear_v(x) ->
+// linear_1; "Quantized weights": int8
 // weights dequantised as q * s, one scale per output channel.)
 //
 // Work split: one wavefront owns a 256-column slab of one matrix of one touched expert

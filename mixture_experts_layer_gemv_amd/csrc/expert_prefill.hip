@@ -1,4 +1,5 @@
-// Expert FFN for large batches (T > 160): grouped W8A16 GEMMs on the MFMA units.
+// Expert FFN for large batches (T > 160), and for expert matrices of at most 2^23 weights at
+// any batch size: grouped W8A16 GEMMs on the MFMA units.
 // (Grok-1 Admin & Architecture Guide, section 3, MoE step 3, the gated GeLU expert
 // gelu(linear(x)) * linear_v(x) -> linear_1; "Quantized weights": int8 weights
 // dequantised as q * s with one scale per output channel, compute in bf16.)

@@ -185,14 +185,16 @@ int run_experts(const uint16_t* x, const int32_t* perm, const int32_t* offsets, 
                 float* y, int splits, int* splits_used, float* gp, int gparts, int T, int d, int f, int E, int k,
                 hipStream_t s) {
   const int rows_cap = T * k;
-  if (T <= moe::kDecodeMaxT) {
+  if (moe::streaming_experts(T, d, f)) {
     MOE_HIP(moe::launch_gate_up_decode(x, perm, offsets, w_gate, w_up, scales, h, gp, gparts, T, k, d, f, E, s),
             "gate_up");
     MOE_HIP(moe::launch_down_decode(h, offsets, w_down, scales, y, splits, rows_cap, T, d, f, E, s), "down");
   } else {
     MOE_HIP(moe::launch_gate_up_prefill(x, perm, offsets, w_gate, w_up, scales, h, rows_cap, d, f, E, s),
             "gate_up");
-    MOE_HIP(moe::launch_down_prefill(h, offsets, w_down, scales, y, splits, rows_cap, d, f, E, splits_used, s),
+    // up to kDecodeMaxT tokens the parts are the host's (no count kept on the device)
+    MOE_HIP(moe::launch_down_prefill(h, offsets, w_down, scales, y, splits, rows_cap, d, f, E,
+                                     T <= moe::kDecodeMaxT ? nullptr : splits_used, s),
             "down");
   }
   return MOE_OK;
@@ -488,7 +490,7 @@ int moe_gate_up(const void* x, const int32_t* perm, const int32_t* offsets, cons
   const auto* xb = static_cast<const uint16_t*>(x);
   const auto* sc = static_cast<const uint16_t*>(scales);
   auto* hh = static_cast<_Float16*>(h);
-  if (T <= moe::kDecodeMaxT) {
+  if (moe::streaming_experts(T, d, f)) {
     // the same split of the contraction as moe_forward; its partial sums live in the
     // library workspace
     const int parts = gate_up_parts(T, d, f, E, k);
@@ -515,7 +517,7 @@ int moe_down(const void* h, const int32_t* offsets, const int8_t* w_down, const 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const auto* hh = static_cast<const _Float16*>(h);
   const auto* sc = static_cast<const uint16_t*>(scales);
-  if (T <= moe::kDecodeMaxT)
+  if (moe::streaming_experts(T, d, f))
     MOE_HIP(moe::launch_down_decode(hh, offsets, w_down, sc, y, splits, T * k, T, d, f, E, s), "down");
   else
     MOE_HIP(moe::launch_down_prefill(hh, offsets, w_down, sc, y, splits, T * k, d, f, E, nullptr, s), "down");

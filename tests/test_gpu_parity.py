@@ -293,7 +293,8 @@ def test_down_stage_parity(name):
 
 
 @pytest.mark.parametrize("kw", [dict(T=8, d=1024, f=2048), dict(T=64, d=768, f=4096, n_pad=9),
-                                dict(T=40, d=1536, f=1024, n_pad=3), dict(T=300, d=1024, f=8192, n_pad=5)])
+                                dict(T=40, d=1536, f=1024, n_pad=3), dict(T=300, d=1024, f=8192, n_pad=5),
+                                dict(T=8, d=1024, f=8448), dict(T=40, d=3072, f=4096, n_pad=3)])
 def test_forward_equals_its_stages_bitwise(kw):
     # moe_forward at T <= 64 routes in two launches (group sums, then routing with the
     # dispatch); the stage entry points run each step on its own. Same arithmetic in the same
@@ -395,10 +396,20 @@ def small_case(name, **kw):
     # about 50 rows; 64 experts x about 9 rows, many tiles idle in their second 32 rows)
     dict(T=200, d=256, f=768, E=16, k=4, n_pad=7),
     dict(T=300, d=512, f=512, E=64, k=2),
-    # few slabs and a long contraction over f: the down projection in 16 parts (T = 1 and T = 3,
-    # the latter with one gate/up wavefront streaming both matrices)
-    dict(T=1, d=256, f=16384),
-    dict(T=3, d=256, f=16384, scale_jitter=True),
+    # few slabs and a long contraction over f (matrices of 2^24 weights: the streaming kernels):
+    # the down projection in 16 parts (T = 1 and T = 3, the latter with one gate/up wavefront
+    # streaming both matrices), 4 experts to keep the weights small
+    dict(T=1, d=512, f=32768, E=4, k=2),
+    dict(T=3, d=512, f=32768, E=4, k=2, scale_jitter=True),
+    # the streaming kernels at 2^23+ weights per matrix: split gate/up contraction (partial sums
+    # and the finish kernel), several 48-row passes behind a biased router, the 65..96-token
+    # switch on both sides, 16- and 32-row passes
+    dict(T=8, d=3072, f=4096, scale_jitter=True),
+    dict(T=40, d=6144, f=2048, n_pad=4),
+    dict(T=160, d=1024, f=8448, E=8, k=2, bias=(3.0, 2.0, 0, 0, 0, 0, 0, 0)),
+    dict(T=80, d=1024, f=8448, E=8, k=2, bias=(3.0, 2.0, 0, 0, 0, 0, 0, 0), n_pad=2),
+    dict(T=70, d=1024, f=8448, n_pad=1),
+    dict(T=12, d=1024, f=8448, x_dist="student4"),
 ])
 def test_layer_edge_shapes(kw):
     inp, d = small_case("edge", **kw)
@@ -527,6 +538,11 @@ def test_doubling_down_scales_doubles_out_exactly(T):
     assert np.max(np.abs(b - 2 * a)) <= 1e-3 * rms(2 * a)
 
 
+# A shape whose expert matrices exceed 2^23 weights, so that up to 160 tokens the streaming
+# kernels run (smaller matrices take the tiled kernels at every batch size).
+SD, SF = 1024, 8448
+
+
 @pytest.mark.parametrize("T", [4, 8, 16, 64, 160])
 def test_kernel_paths_agree_across_a_boundary(T):
     # T tokens, then the same tokens plus one padded token. At 4 | 5 gate/up goes from one
@@ -534,15 +550,22 @@ def test_kernel_paths_agree_across_a_boundary(T):
     # (down) the streaming kernels go from 16- to 32-row passes and at 64 | 65 from 32- to
     # 48-row passes (each row's MFMA sequence is unchanged: the same bits); at 160 | 161 the
     # tiled kernels take over (the real rows agree to the output tolerance)
-    inp, d = small_case("paths", T=T + 1, d=512, f=768, n_pad=0)
-    a, _ = run_forward(dict(d, x=d["x"][:T].contiguous()), T, 512, 768, 8, 2)
+    inp, d = small_case("paths", T=T + 1, d=SD, f=SF, n_pad=0)
+    a, _ = run_forward(dict(d, x=d["x"][:T].contiguous()), T, SD, SF, 8, 2)
     pad = torch.ones(T + 1, dtype=torch.uint8, device="cuda")
     pad[T] = 0
-    b, _ = run_forward(dict(d, pad_mask=pad), T + 1, 512, 768, 8, 2)
+    b, _ = run_forward(dict(d, pad_mask=pad), T + 1, SD, SF, 8, 2)
     if T < 160:
-        assert moe.down_splits(T, 512, 768, 8, 2) == moe.down_splits(T + 1, 512, 768, 8, 2)
+        assert moe.down_splits(T, SD, SF, 8, 2) == moe.down_splits(T + 1, SD, SF, 8, 2)
         assert np.array_equal(a, b[:T])
     assert np.max(np.abs(a - b[:T])) <= 1e-3 * rms(a)
+
+
+@pytest.mark.parametrize("T", [8, 64, 160])
+def test_small_matrices_take_the_tiled_kernels(T):
+    # Expert matrices of at most 2^23 weights run in the tiled kernels at every batch size;
+    # their parity with the oracle, padded rows included
+    check_layer(*small_case("small_tiled", T=T, d=512, f=768, n_pad=3), label=f"tiled T={T}")
 
 
 def test_tile_heights_agree_bitwise():
