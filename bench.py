@@ -252,8 +252,12 @@ def main() -> int:
         return 0
 
     work = algorithmic_work(spec, counts)
-    decode = T <= 64
-    if decode:
+    # The library's kernel choice (csrc/launch_policy.h, expert_prefill.hip): the streaming
+    # kernels up to 160 tokens when an expert matrix holds more than 2^23 weights, else the
+    # tiled ones, in 128-row tiles when at most 96 rows per expert are possible.
+    streaming = T <= 160 and d * f > (1 << 23)
+    bm = 128 if T * k <= 96 * E else 256
+    if streaming:
         gu_ach = work["gu_bytes"] / (gu_ms * 1e-3) / 1e9
         dn_ach = work["dn_bytes"] / (dn_ms * 1e-3) / 1e9
         rec = recorded_traffic(args.workload, "mixture_experts_layer_gemv_amd/csrc/expert_decode.hip")
@@ -276,10 +280,10 @@ def main() -> int:
                 "frac": round(gu_ach / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": rec["gate_up_traffic_bytes"] if rec else None,
                 "traffic_source": rec["profile"] if rec else None,
-                "kernel": "expert_prefill_kernel<true, 256>", "algorithmic_flops_per_launch": work["gu_flops"],
+                "kernel": f"expert_prefill_kernel<true, {bm}>", "algorithmic_flops_per_launch": work["gu_flops"],
                 "algorithmic_bytes_per_launch": work["gu_bytes_prefill"], "avg_launch_ms": round(gu_ms, 5)}
         layer_tf = work["layer_flops"] / (ms_per_step * 1e-3) / 1e12
-        kern = {"expert_prefill_kernel<false, 256>": {"avg_launch_ms": round(dn_ms, 5), "achieved_TFLOPs": round(dn_ach, 1),
+        kern = {f"expert_prefill_kernel<false, {bm}>": {"avg_launch_ms": round(dn_ms, 5), "achieved_TFLOPs": round(dn_ach, 1),
                                                  "frac": round(dn_ach / MFMA_BF16_PEAK_TFLOPS, 4)},
                 "layer": {"TFLOPs": round(layer_tf, 1), "mfma_frac": round(layer_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                           "algorithmic_flops": work["layer_flops"]}}
