@@ -252,11 +252,8 @@ def main() -> int:
         return 0
 
     work = algorithmic_work(spec, counts)
-    # The library's kernel choice (csrc/launch_policy.h, expert_prefill.hip): the streaming
-    # kernels up to 160 tokens when an expert matrix holds more than 2^23 weights, else the
-    # tiled ones, in 128-row tiles when at most 96 rows per expert are possible.
-    streaming = T <= 160 and d * f > (1 << 23)
-    bm = 128 if T * k <= 96 * E else 256
+    bm = moe.expert_kernels(T, d, f, E, k)  # 0: streaming kernels, else tiled with bm-row tiles
+    streaming = bm == 0
     if streaming:
         gu_ach = work["gu_bytes"] / (gu_ms * 1e-3) / 1e9
         dn_ach = work["dn_bytes"] / (dn_ms * 1e-3) / 1e9

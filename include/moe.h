@@ -145,6 +145,13 @@ int moe_down(const void* h, const int32_t* offsets, const int8_t* w_down, const 
              float* y, int splits, int T, int d, int f, int E, int k, void* stream);
 int moe_down_splits(int T, int d, int f, int E, int k);
 
+/* Which expert kernels moe_forward, moe_gate_up and moe_down run for a shape: 0 = the
+   weight-streaming kernels (T <= 160 and more than 2^23 weights per expert matrix), else the
+   row height of the tiled MFMA kernels' tiles, 128 (at most 96 assignments per expert on
+   average) or 256. -1 for a shape the library rejects (moe_last_error() says why). Host only:
+   no device call, no allocation. */
+int moe_expert_kernels(int T, int d, int f, int E, int k);
+
 /* Step 4: out[t] = sum over j of topk_w[t][j] * (sum over parts s of y[s][pos[t][j]]),
    parts in order, slots in order, fp32; +0.0 rows for padded tokens. */
 int moe_combine(const float* y, int splits, const int32_t* pos, const float* topk_w,

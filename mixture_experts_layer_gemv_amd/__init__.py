@@ -30,6 +30,7 @@ SIGNATURES = {
     "moe_gate_up": ([_vp] * 7 + [_i32] * 5 + [_vp], _i32),
     "moe_down": ([_vp] * 5 + [_i32] * 6 + [_vp], _i32),
     "moe_down_splits": ([_i32] * 5, _i32),
+    "moe_expert_kernels": ([_i32] * 5, _i32),
     "moe_combine": ([_vp] + [_i32] + [_vp] * 4 + [_i32] * 3 + [_vp], _i32),
     "moe_workspace_bytes": ([_i32] * 5, _sz),
     "moe_forward_dense": ([_vp] * 8 + [_i32] * 5 + [_vp, _vp, _vp, _sz], _i32),
@@ -111,6 +112,11 @@ def workspace_bytes(T: int, d: int, f: int, E: int, k: int) -> int:
 
 def down_splits(T: int, d: int, f: int, E: int, k: int) -> int:
     return lib().moe_down_splits(T, d, f, E, k)
+
+
+def expert_kernels(T: int, d: int, f: int, E: int, k: int) -> int:
+    """0: the streaming expert kernels run; 128 / 256: the tiled ones, with tiles of that many rows."""
+    return lib().moe_expert_kernels(T, d, f, E, k)
 
 
 def release_workspace() -> None:

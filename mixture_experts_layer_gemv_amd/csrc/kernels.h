@@ -59,6 +59,9 @@ hipError_t launch_down_decode(const _Float16* H, const int32_t* offsets, const i
                               const uint16_t* scales, float* Y, int splits, int rows_cap, int T,
                               int d, int f, int E, hipStream_t stream);
 
+// Row height (128 or 256) of the tiled kernels' m-tiles for rows_cap = T * k assignments.
+int prefill_bm(int rows_cap, int E);
+
 hipError_t launch_gate_up_prefill(const uint16_t* x, const int32_t* perm, const int32_t* offsets,
                                   const int8_t* w_gate, const int8_t* w_up, const uint16_t* scales,
                                   _Float16* H, int rows_cap, int d, int f, int E, hipStream_t stream);

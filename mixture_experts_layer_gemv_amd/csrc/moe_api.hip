@@ -237,6 +237,11 @@ int moe_down_splits(int T, int d, int f, int E, int k) {
   return down_splits(T, d, f, E, k);
 }
 
+int moe_expert_kernels(int T, int d, int f, int E, int k) {
+  if (check_shape(T, d, f, E, k) != MOE_OK) return -1;
+  return moe::streaming_experts(T, d, f) ? 0 : moe::prefill_bm(T * k, E);
+}
+
 void moe_release_workspace(void) {
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   int cur = 0;

@@ -123,6 +123,21 @@ def test_workspace_size_and_split_policy():
     assert moe.workspace_bytes(8, 6144, 32768, 8, 9) == 0
 
 
+def test_expert_kernel_choice():
+    # streaming kernels to 160 tokens only for expert matrices above 2^23 weights
+    assert moe.expert_kernels(8, 6144, 32768, 8, 2) == 0
+    assert moe.expert_kernels(160, 6144, 32768, 8, 2) == 0
+    assert moe.expert_kernels(161, 6144, 32768, 8, 2) == 128
+    assert moe.expert_kernels(384, 6144, 32768, 8, 2) == 128
+    assert moe.expert_kernels(385, 6144, 32768, 8, 2) == 256
+    assert moe.expert_kernels(8192, 6144, 32768, 8, 2) == 256
+    assert moe.expert_kernels(8, 6144, 4096, 8, 2) == 0
+    assert moe.expert_kernels(64, 256, 512, 8, 2) == 128
+    assert moe.expert_kernels(160, 2048, 4096, 8, 2) == 128
+    assert moe.expert_kernels(160, 2048, 4096 + 256, 8, 2) == 0
+    assert moe.expert_kernels(8, 6144, 32768, 8, 0) == -1
+
+
 def test_forward_ex_rejects_small_or_misaligned_workspace():
     lib = moe.lib()
     need = moe.workspace_bytes(8, 256, 512, 8, 2)
