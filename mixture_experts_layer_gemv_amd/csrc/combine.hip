@@ -4,7 +4,7 @@
 //   y_(t,j)[c] = sum over parts s (in order) of Y[s][pos[t][j]][c],
 // fp32, a fixed order per element, so the result is deterministic. Padded tokens (and
 // slots with pos < 0) contribute nothing; padded rows are +0.0.
-// grid (T, ceil(d / (4 * block))), block 64 (T <= 64) or 256: each thread writes 4 adjacent
+// grid (T, ceil(d / (4 * block))), block 64 (T <= 160) or 256: each thread writes 4 adjacent
 // columns.
 #include "device_common.h"
 #include "kernels.h"

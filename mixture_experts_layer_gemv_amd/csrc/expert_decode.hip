@@ -2,8 +2,8 @@
 // layer streams the int8 weights of the experts it touches once from HBM, so these
 // kernels are built for bytes in flight, not for reuse. (Grok-1 Admin & Architecture
 // Guide, section 3, MoE step 3: the gated GeLU expert gelu(linear(x)) * linear_v(x) ->
-// linear_1; "Quantized weights": int8
-// weights dequantised as q * s, one scale per output channel.)
+// linear_1; "Quantized weights": int8 weights dequantised as q * s, one scale per output
+// channel.)
 //
 // Work split: one wavefront owns a 256-column slab of one matrix of one touched expert
 // and runs down the whole contraction, or one of `splits` parts of it when the slabs

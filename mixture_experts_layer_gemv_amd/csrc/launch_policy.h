@@ -1,8 +1,8 @@
-// Launch policy of the expert kernels: how many parts the contractions are split into. The
-// decode kernels (T <= 64) stream each touched expert's weights once; a split only adds
-// wavefronts (and fp32 partial sums) when the 256-column slabs alone would leave the chip
-// under-filled, e.g. at one GPU's share of a tensor-parallel split over f. The prefill down
-// kernel splits to fill a ragged last round of workgroups.
+// Launch policy of the expert kernels: which kernels run and how many parts the contractions
+// are split into. The streaming kernels (T <= 160) read each touched expert's weights once
+// per pass; a split only adds wavefronts (and fp32 partial sums) when the 256-column slabs
+// alone would leave the chip under-filled, e.g. at one GPU's share of a tensor-parallel
+// split over f. The prefill down kernel splits to fill a ragged last round of workgroups.
 #pragma once
 
 #include <algorithm>
@@ -19,7 +19,7 @@ namespace moe {
 // tokens; at 2^24 the streaming kernels are ahead again up to 128 tokens.
 inline bool streaming_experts(int T, int d, int f) { return T <= kDecodeMaxT && (long)d * f > (1L << 23); }
 
-// Small batches (T <= 64), targets measured on whole forward passes at the Grok-1 shape and
+// Small batches (T <= 160), targets measured on whole forward passes at the Grok-1 shape and
 // at one GPU's tensor-parallel share: the down projection wants about 768 workgroups while
 // each wavefront carries one 16-row tile (T <= 16: one wavefront per SIMD with a 4-step load
 // ring, so that all of them are resident at once) and about 512 with two (longer streams win
