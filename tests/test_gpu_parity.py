@@ -375,21 +375,18 @@ def small_case(name, **kw):
     dict(T=96, d=512, f=256, E=8, k=2, n_pad=10),
     dict(T=33, d=768, f=1024, E=8, k=2, x_dist="student4"),
     dict(T=1000, d=256, f=768, E=8, k=2, bias=(3.0, 2.0, 0, 0, 0, 0, 0, 0)),
-    # narrow f at decode: the gate/up contraction split in 2 (one 16-row tile) or 4 parts
-    # (two tiles, padded), the down contraction split in 2
+    # expert matrices of at most 2^23 weights take the tiled kernels at every batch size:
+    # narrow f at decode (one down part, or 2 at d = 1536, f = 2048)
     dict(T=8, d=3072, f=1024, E=8, k=2, scale_jitter=True),
     dict(T=40, d=6144, f=512, E=8, k=2, n_pad=4),
     dict(T=8, d=1536, f=2048, E=8, k=2, x_dist="student4"),
-    # one or two tokens reach at most 2 or 4 experts: the gate/up contraction split in 8 parts
+    # one or two tokens reach at most 2 or 4 experts
     dict(T=1, d=6144, f=1024, E=8, k=2),
     dict(T=2, d=3072, f=512, E=8, k=2, scale_jitter=True),
-    # 65..160 tokens: the streaming kernels in 48-row passes; with the gate/up split (narrow f),
-    # and with a biased router that sends one expert over 48 rows (several passes)
+    # 65..160 tokens in 128-row tiles, narrow (at most 64 rows) or not, behind a biased router
     dict(T=100, d=6144, f=1024, E=8, k=2, n_pad=6),
     dict(T=160, d=256, f=512, E=8, k=2, bias=(3.0, 2.0, 0, 0, 0, 0, 0, 0)),
-    # 65..96 tokens: the 32-row kernels run unless an expert exceeds 32 rows (the 65-token cases
-    # above), then the 48-row ones (a biased router sends 76 of 78 tokens to expert 0; 96
-    # unbiased tokens give one expert 34 rows)
+    # a biased router sends 76 of 78 tokens to expert 0; 96 unbiased tokens give one expert 34 rows
     dict(T=80, d=256, f=512, E=8, k=2, bias=(3.0, 2.0, 0, 0, 0, 0, 0, 0), n_pad=2),
     dict(T=96, d=512, f=768, E=8, k=2, n_pad=3),
     # above 160 tokens with many experts: 128-row tiles, most of them narrow (16 experts x
@@ -401,6 +398,11 @@ def small_case(name, **kw):
     # streaming both matrices), 4 experts to keep the weights small
     dict(T=1, d=512, f=32768, E=4, k=2),
     dict(T=3, d=512, f=32768, E=4, k=2, scale_jitter=True),
+    # the tiled down kernel split in 2 parts of 18 slices (not a multiple of 4), 8 parts and 16
+    # parts (one token, one 256-column slab per expert, 2^23 weights per matrix)
+    dict(T=8, d=1024, f=2304, E=8, k=2, n_pad=1),
+    dict(T=8, d=1024, f=8192, E=8, k=2, scale_jitter=True),
+    dict(T=1, d=256, f=32768, E=4, k=2),
     # the streaming kernels at 2^23+ weights per matrix: split gate/up contraction (partial sums
     # and the finish kernel), several 48-row passes behind a biased router, the 65..96-token
     # switch on both sides, 16- and 32-row passes
