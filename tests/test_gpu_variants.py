@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_helpers import OUT_TOL, exclusions, rms, sample_rows, to_dev
+from gpu_helpers import OUT_TOL, exclusions, max_excluded, rms, sample_rows, to_dev
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -96,6 +96,20 @@ def test_graph_replays_match_eager(case):
             got = out.cpu().numpy()
             eager = sparse_out(dict(d, x=x), s)
             assert np.array_equal(got, eager), rep
+            if rep == 0:
+                # the first replay runs on the workload's own inputs: against the oracle too
+                r = oracle.route(inp["x"], inp["router_w"], inp["router_bias"], inp["pad_mask"], s.k)
+                excl, _ = exclusions(r)
+                assert int(excl.sum()) <= max_excluded(s.T)
+                pads = None if inp["pad_mask"] is None else np.nonzero(inp["pad_mask"] == 0)[0][:2]
+                rows = sample_rows(s.T, 24, seed=9, must=pads)
+                ref, _, _ = oracle.forward_inputs(inp, k=s.k, rows=rows)
+                keep = ~excl[rows]
+                ratio = float(np.max(np.abs(got[rows][keep] - ref[keep])) / rms(ref))
+                print(f"graph {case}: replay 0 vs oracle max|err|/rms = {ratio:.3e} on {len(rows)} rows", flush=True)
+                assert ratio <= OUT_TOL
+                if inp["pad_mask"] is not None:
+                    assert np.all(got[inp["pad_mask"] == 0] == 0)
     finally:
         g.close()
 

@@ -120,6 +120,64 @@ def test_top_k_equals_brute_force_enumeration():
                 assert list(got).index(1) < list(got).index(2)  # equal p: lower index first
 
 
+def gaps_from_sorted(probs, k, real):
+    """The selection and order gaps of each token from numpy's descending sort of its
+    probabilities: sel = p_(k) - p_(k+1), order = min over j < k of p_(j) - p_(j+1)
+    (1-based ranks; +inf where undefined or padded), in fp32 as the oracle computes them."""
+    T, E = probs.shape
+    s = -np.sort(-probs, axis=1)  # descending, fp32
+    sel = np.full(T, np.inf, np.float32)
+    order = np.full(T, np.inf, np.float32)
+    if k < E:
+        sel = (s[:, k - 1] - s[:, k]).astype(np.float32)
+    if k > 1:
+        order = np.min(s[:, : k - 1] - s[:, 1:k], axis=1).astype(np.float32)
+    sel[~real] = np.inf
+    order[~real] = np.inf
+    return sel, order
+
+
+@pytest.mark.parametrize("k,E", [(1, 4), (2, 4), (3, 4), (4, 4), (1, 8), (2, 8), (3, 8), (4, 8)])
+def test_near_tie_gaps_equal_sorted_probability_differences(k, E):
+    # gap_sel decides which tokens the GPU parity leaves out, so it must be the distance between
+    # the k-th and (k+1)-th largest probabilities, not a neighbouring pair: numpy's sort of the
+    # same fp32 probabilities gives the same differences bit for bit (an off-by-one in the rank,
+    # e.g. p_(k-1) - p_(k), fails on general inputs, where x = 0 cannot tell them apart)
+    inp = small(f"gaps-{k}-{E}", T=400, d=64, E=E, k=k, n_pad=13, x_dist="student4")
+    r = oracle.route(inp["x"], inp["router_w"], None, inp["pad_mask"], k=k)
+    real = inp["pad_mask"] != 0
+    sel, order = gaps_from_sorted(r["probs"], k, real)
+    assert np.array_equal(r["gap_sel"], sel)
+    assert np.array_equal(r["gap_order"], order)
+    assert np.all(r["gap_sel"][real] >= 0) and np.all(r["gap_order"][real] >= 0)
+    if k < E:
+        # the selection gap is the distance from the last selected weight to the best rejected one
+        others = r["probs"].copy()
+        np.put_along_axis(others, np.maximum(r["ids"], 0), -1, 1)
+        assert np.array_equal(r["gap_sel"][real], (r["w"][:, k - 1] - others.max(1))[real])
+
+
+def test_near_tie_gaps_closed_form():
+    # One-hot x picks one router row: the logits are exactly log(q) for a chosen distribution
+    # q = (0.05, 0.4, 0.1, 0.3, 0.15) (in a shuffled expert order), so p = q up to fp32 rounding
+    # and every gap is known: sorted 0.4, 0.3, 0.15, 0.1, 0.05 ->
+    #   k = 1: sel 0.1, order inf; k = 2: sel 0.15, order 0.1; k = 3: sel 0.05, order 0.1;
+    #   k = 4: sel 0.05, order 0.05; k = 5 = E: sel inf
+    q = np.array([0.05, 0.4, 0.1, 0.3, 0.15])
+    d = 8
+    wr = np.zeros((d, 5), np.float32)
+    wr[3] = np.log(q).astype(np.float32)
+    x = np.zeros((1, d), np.uint16)
+    x[0, 3] = synth.f32_to_bf16_bits(np.float32([1.0]))[0]
+    expect = {1: (0.1, np.inf), 2: (0.15, 0.1), 3: (0.05, 0.1), 4: (0.05, 0.05), 5: (np.inf, 0.05)}
+    for k, (sel, order) in expect.items():
+        r = oracle.route(x, wr, None, None, k=k)
+        assert np.allclose(r["probs"][0], q, rtol=1e-6)
+        assert r["ids"][0].tolist() == [1, 3, 4, 2, 0][:k]
+        for got, want in ((r["gap_sel"][0], sel), (r["gap_order"][0], order)):
+            assert (np.isinf(got) and np.isinf(want)) or abs(got - want) <= 1e-6, (k, got, want)
+
+
 def test_routing_weights_are_unrenormalised_top2_probabilities(tiny_inputs):
     r = oracle.route(tiny_inputs["x"], tiny_inputs["router_w"], None, None, k=2)
     w, p, ids = r["w"], r["probs"], r["ids"]
