@@ -18,19 +18,24 @@ from typing import Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# MOE_ORACLE_LIB: load another build of the oracle (the sanitizer test's)
+_LIB_PATH = os.environ.get("MOE_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
-def build(verbose: bool = False) -> str:
-    """Compile liboracle.so with g++ (-ffp-contract=off: no fused multiply-add)."""
+def build(verbose: bool = False, out: Optional[str] = None, sanitize: bool = False) -> str:
+    """Compile liboracle.so with g++ (-ffp-contract=off: no fused multiply-add); `sanitize` adds
+    AddressSanitizer and UndefinedBehaviorSanitizer, written to `out`."""
     src = os.path.join(_HERE, "moe_oracle.cpp")
-    cmd = ["g++", "-O3", "-mavx2", "-ffp-contract=off", "-fno-fast-math", "-std=c++17", "-fPIC",
-           "-shared", "-pthread", src, "-o", _LIB_PATH]
+    out = out or os.path.join(_HERE, "liboracle.so")
+    san = ["-g", "-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=undefined"] \
+        if sanitize else []
+    cmd = ["g++", "-O3", *san, "-mavx2", "-ffp-contract=off", "-fno-fast-math", "-std=c++17", "-fPIC",
+           "-shared", "-pthread", src, "-o", out]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    return _LIB_PATH
+    return out
 
 
 def _load():

@@ -310,8 +310,9 @@ int oracle_forward(const uint16_t* x, const float* router_w, const float* router
       o[c] = acc;
     }
   }
-  if (ids_out) std::memcpy(ids_out, ids.data(), sizeof(int32_t) * ids.size());
-  if (w_out) std::memcpy(w_out, w.data(), sizeof(float) * w.size());
+  // (an empty batch copies nothing: memcpy may not be handed the NULL data() of an empty vector)
+  if (ids_out && !ids.empty()) std::memcpy(ids_out, ids.data(), sizeof(int32_t) * ids.size());
+  if (w_out && !w.empty()) std::memcpy(w_out, w.data(), sizeof(float) * w.size());
   return 0;
 }
 
@@ -488,7 +489,7 @@ int oracle_block_forward(const uint16_t* h, const float* norm_pre, const float* 
     oracle_rms_norm_row(&m[(size_t)t * d], norm_post, eps, d, nrm.data());
     for (int i = 0; i < d; ++i) h_out[(size_t)t * d + i] = bf16_value(h[(size_t)t * d + i]) + nrm[i];
   }
-  if (x_out) std::memcpy(x_out, x.data(), sizeof(uint16_t) * x.size());
+  if (x_out && !x.empty()) std::memcpy(x_out, x.data(), sizeof(uint16_t) * x.size());
   return 0;
 }
 

@@ -34,23 +34,28 @@ from typing import Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libsynth.so")
+# MOE_SYNTH_LIB: load another build of the generator (the sanitizer test's)
+_LIB_PATH = os.environ.get("MOE_SYNTH_LIB") or os.path.join(_HERE, "libsynth.so")
 _lib = None
 
 TENSOR_X, TENSOR_WR, TENSOR_QG, TENSOR_QU, TENSOR_QD, TENSOR_PAD, TENSOR_SCALE = 1, 2, 3, 4, 5, 6, 7
 DEFAULT_SEED = 42
 
 
-def build(verbose: bool = False) -> str:
-    """Compile libsynth.so with gcc (OpenMP for bulk fills)."""
+def build(verbose: bool = False, out: Optional[str] = None, sanitize: bool = False) -> str:
+    """Compile libsynth.so with gcc (OpenMP for bulk fills); `sanitize` adds AddressSanitizer and
+    UndefinedBehaviorSanitizer (host code only), written to `out`."""
     import subprocess
 
     src = os.path.join(_HERE, "synth.c")
-    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c11", src, "-o", _LIB_PATH, "-lm"]
+    out = out or os.path.join(_HERE, "libsynth.so")
+    san = ["-g", "-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=undefined"] \
+        if sanitize else []
+    cmd = ["gcc", "-O2", *san, "-fPIC", "-shared", "-fopenmp", "-std=c11", src, "-o", out, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    return _LIB_PATH
+    return out
 
 
 def _load():
