@@ -17,6 +17,11 @@ namespace moe {
 // the tiled kernels run them in narrow tiles over many more workgroups: d = 256, f = 512 at
 // 64 tokens 39 -> 30 us per forward, d = 2048, f = 4096 (2^23) 3-29% faster from 8 to 160
 // tokens; at 2^24 the streaming kernels are ahead again up to 128 tokens.
+// Accepted trade-off: from 129 to 160 tokens a batch whose largest expert exceeds 48 rows
+// takes a second streaming pass over that expert's weights; where the slabs fill only about
+// one round of wavefronts (e.g. d = 4096, f = 8192 or f = 16384) the tiled kernels are then
+// faster (311 vs 213 us and 546 vs 410 us at 160 tokens), but the host cannot see the row
+// counts, and the Grok-1 shape and its tensor-parallel share do not lose there.
 inline bool streaming_experts(int T, int d, int f) { return T <= kDecodeMaxT && (long)d * f > (1L << 23); }
 
 // Small batches (T <= 160), targets measured on whole forward passes at the Grok-1 shape and
