@@ -302,7 +302,8 @@ __global__ __launch_bounds__(kThreads) void expert_prefill_kernel(
     }
   };
 
-  // slices it (even) and it + 1 (odd) per trip; nslices is a multiple of 4. The loads and
+  // slices it (even) and it + 1 (odd) per trip; nslices is even (the launchers reject a
+  // contraction part that is not a multiple of 128). The loads and
   // stores are unconditional (past the end they re-read the last slice into a buffer that
   // is not read again): a conditional load would make the compiler's wait counts at the
   // stores assume the path without it, i.e. wait for the loads just issued.
@@ -537,6 +538,9 @@ TileOrder make_order(int nslots, int ntiles, int xn_pref) {
 hipError_t launch_gate_up_prefill(const uint16_t* x, const int32_t* perm, const int32_t* offsets,
                                   const int8_t* w_gate, const int8_t* w_up, const uint16_t* scales,
                                   _Float16* H, int rows_cap, int d, int f, int E, hipStream_t stream) {
+  // the main loop takes two 64-deep slices per trip: an odd slice count would multiply the
+  // re-read last slice twice
+  if (d % (2 * BK) != 0 || f % HALF != 0) return hipErrorInvalidValue;
   const int bm = prefill_bm(rows_cap, E);
   const int nslots = prefill_mslots(rows_cap, E, bm), ntiles = f / HALF;
   // the activations fit the last-level cache: every XCD takes its own weight columns
@@ -552,6 +556,9 @@ hipError_t launch_down_prefill(const _Float16* H, const int32_t* offsets, const 
                                const uint16_t* scales, float* Y, int splits, int rows_cap, int d,
                                int f, int E, int* splits_used, hipStream_t stream) {
   if (splits_used != nullptr && splits != 2 && splits != 4) return hipErrorInvalidValue;
+  // every part, and every part the kernel may keep (1 or 2 of 2; 1, 2 or 4 of 4), is a whole
+  // number of 128-deep trips of the main loop, and the columns are whole 256-column tiles
+  if (splits < 1 || f % (splits * 2 * BK) != 0 || d % (2 * HALF) != 0) return hipErrorInvalidValue;
   const int bm = prefill_bm(rows_cap, E);
   const int nslots = prefill_mslots(rows_cap, E, bm), ntiles = d / (2 * HALF);
   // every XCD takes its own weight columns, as for gate/up (measured against 2 x 4 and 4 x 2
