@@ -2,19 +2,24 @@
 """Throughput of the Grok-1 top-2-of-8 MoE layer forward pass on one MI355X.
 
 One step = one moe_forward call (router, dispatch, gate/up + GeGLU, down, combine) over
-one batch of seeded synthetic inputs already resident in HBM. Default workload: the
-Grok-1-shape decode batch (T=8, d=6144, f=32768, E=8, k=2, int8 expert weights with
-per-output-channel bf16 scales). Prints ONE JSON line on stdout; progress goes to stderr.
+one batch of seeded synthetic inputs already resident in HBM. The headline workload is
+the Grok-1-shape decode batch (T=8, d=6144, f=32768, E=8, k=2, int8 expert weights with
+per-output-channel bf16 scales); the same JSON line carries the other four workloads the
+metric is defined on (the tiny layer, batched decode, prefill, skewed routing) under
+"configs", each with its own timing, roofline and CPU-oracle baseline. Prints ONE JSON
+line on stdout; progress goes to stderr.
 
-Besides the step time it reports, for the dominant kernel (gate/up + GeGLU), achieved
-algorithmic bandwidth (decode) or MFMA throughput (prefill) from HIP events recorded on
-the launch stream around that kernel, and the CPU oracle timed on a bounded sample.
+For the dominant kernel (gate/up + GeGLU) of each workload it reports achieved algorithmic
+bandwidth (streaming kernels, decode) or MFMA throughput (tiled kernels, prefill) from HIP
+events recorded on the launch stream around that kernel, and the CPU oracle timed on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -26,10 +31,32 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s; % HBM peak (decode T<=64), % MFMA peak (prefill)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
+WORKLOADS = ["tiny", "decode", "batched_decode", "prefill", "skewed", "decode_tp8", "prefill_tp8"]
+# the five workloads the metric is defined on; the first after the headline are reported under "configs"
+METRIC_WORKLOADS = ["tiny", "decode", "batched_decode", "prefill", "skewed"]
+# the GPU machine gives one GPU's process a share of 16 host cores, whatever the host has in all
+HOST_CORE_SHARE = 16
 
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def host_info() -> dict:
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
+    return {"cpu_model": model, "hardware_concurrency": os.cpu_count(), "affinity_cpus": affinity,
+            "oracle_threads": max(1, min(affinity, HOST_CORE_SHARE))}
 
 
 def algorithmic_work(spec, counts):
@@ -108,15 +135,231 @@ def copy_calibration(nbytes: int, steps: int, warmup: int) -> int:
     return 0
 
 
+class Inputs:
+    """Host inputs of a workload and their device copies (the Grok-shape workloads share one
+    weight set, uploaded once)."""
+
+    _weights: dict = {}
+
+    def __init__(self, name: str):
+        import numpy as np
+        import torch
+
+        import synth
+
+        self.spec = s = synth.CONFIGS[name]
+        dev = torch.device("cuda:0")
+        to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+        bf = lambda a: to(a.view(np.int16)).view(torch.bfloat16)  # noqa: E731
+        t0 = time.time()
+        wkey = (s.d, s.f, s.E, s.w_set, s.f_full)
+        if wkey not in Inputs._weights:
+            Inputs._weights.clear()  # keep one weight set resident at a time
+            host = {n: synth.expert_weights(s, n.split("_")[1]) for n in ("w_gate", "w_up", "w_down")}
+            host["router_w"] = synth.router_w(s)
+            host["scales"] = synth.scales(s)
+            devw = {n: to(host[n]) for n in ("w_gate", "w_up", "w_down", "router_w")}
+            devw["scales"] = bf(host["scales"])
+            Inputs._weights[wkey] = (host, devw)
+        host, devw = Inputs._weights[wkey]
+        self.inp = synth.make_inputs(s, with_weights=False)
+        self.inp.update({n: host[n] for n in ("w_gate", "w_up", "w_down", "router_w", "scales")})
+        self.x, self.wr, self.sc = bf(self.inp["x"]), devw["router_w"], devw["scales"]
+        self.wg, self.wu, self.wd = devw["w_gate"], devw["w_up"], devw["w_down"]
+        self.pad = None if self.inp["pad_mask"] is None else to(self.inp["pad_mask"])
+        self.bias = None if self.inp["router_bias"] is None else to(self.inp["router_bias"])
+        self.out = torch.empty((s.T, s.d), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        log(f"{name}: inputs resident in HBM after {time.time() - t0:.1f}s")
+
+
+def timed_steps(step, steps: int, stream) -> dict:
+    """Exactly `steps` calls of step() between two synchronisations, with a HIP event on the
+    launch stream before each call and after the last: mean (the headline), median and min."""
+    import torch
+
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return {"ms_per_step": evs[0].elapsed_time(evs[steps]) / steps, "ms_median": statistics.median(per),
+            "ms_min": min(per)}
+
+
+def cpu_baseline(wl: Inputs, seconds: float, threads: int, name: str):
+    """The oracle as it stands on a bounded sample of the workload's token rows (all rows up
+    to 16 tokens, else 16 seeded rows, repeated until `seconds` of wall time)."""
+    import numpy as np
+
+    import oracle
+
+    T, k = wl.spec.T, wl.spec.k
+    rows = np.arange(T) if T <= 16 else np.sort(np.random.default_rng(0).choice(T, 16, replace=False))
+    reps, tok, t_start = 0, 0, time.time()
+    while True:
+        oracle.forward_inputs(wl.inp, k=k, nthreads=threads, rows=rows)
+        reps += 1
+        tok += len(rows)
+        if time.time() - t_start >= seconds or reps >= 1000:
+            break
+    el = time.time() - t_start
+    return {"value": round(tok / el, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} oracle forward(s) of {len(rows)} token rows of the {name} workload "
+                      f"({el:.1f} s wall, fp32, {threads} threads)"}
+
+
+def measure(name: str, args, host: dict, cpu_seconds: float, graph: bool) -> dict:
+    """Staged per-kernel timing, then warm-up and K timed forward steps of one workload."""
+    import torch
+
+    import mixture_experts_layer_gemv_amd as moe
+
+    wl = Inputs(name)
+    s = wl.spec
+    T, d, f, E, k = s.T, s.d, s.f, s.E, s.k
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    counts_t = torch.empty(E, dtype=torch.int32, device=dev)
+
+    def step(dbg=None):
+        moe.moe_forward_ex(wl.x, wl.wr, wl.wg, wl.wu, wl.wd, wl.sc, wl.pad, wl.out, T, d, f, E, k, stream,
+                           router_bias=wl.bias, dbg=dbg)
+
+    step(dbg={"counts": counts_t})  # grows the library workspace (synchronising), outside timing
+    torch.cuda.synchronize()
+    counts = counts_t.cpu().tolist()
+
+    # ---- per-kernel durations first (from idle the GPU needs ~15 ms of work to reach its
+    #      steady clocks): the same kernels through the stage entry points, HIP events on the
+    #      launch stream around the two expert kernels
+    tk = T * k
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(max(tk, 1), dtype=torch.int32, device=dev)
+    pos = torch.empty((T, k), dtype=torch.int32, device=dev)
+    h = torch.empty((tk, f), dtype=torch.float16, device=dev)
+    splits = moe.down_splits(T, d, f, E, k)
+    y = torch.empty((splits, tk, d), dtype=torch.float32, device=dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def staged(e=None):
+        moe.moe_route(wl.x, wl.wr, wl.bias, wl.pad, ids, wts, T, d, E, k, stream)
+        moe.moe_dispatch(ids, wl.pad, counts_t, offsets, perm, pos, T, E, k, stream)
+        if e:
+            e[0].record(stream)
+        moe.moe_gate_up(wl.x, perm, offsets, wl.wg, wl.wu, wl.sc, h, T, d, f, E, k, stream)
+        if e:
+            e[1].record(stream)
+            e[2].record(stream)
+        moe.moe_down(h, offsets, wl.wd, wl.sc, y, splits, T, d, f, E, k, stream)
+        if e:
+            e[3].record(stream)
+        moe.moe_combine(y, splits, pos, wts, wl.pad, wl.out, T, d, k, stream)
+
+    for _ in range(max(20, args.warmup)):
+        staged()
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        staged(evs[i])
+    torch.cuda.synchronize()
+    gu_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    dn_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    log(f"{name}: gate_up {gu_ms:.4f} ms, down {dn_ms:.4f} ms (splits={splits})")
+    del h, y
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # ---- timed region: exactly K steps
+    t = timed_steps(step, args.steps, stream)
+    log(f"{name}: {args.steps} steps: {t['ms_per_step']:.4f} ms/step (median {t['ms_median']:.4f}, "
+        f"min {t['ms_min']:.4f})")
+
+    work = algorithmic_work(s, counts)
+    bm = moe.expert_kernels(T, d, f, E, k)  # 0: streaming kernels, else tiled with bm-row tiles
+    if bm == 0:
+        gu_ach = work["gu_bytes"] / (gu_ms * 1e-3) / 1e9
+        dn_ach = work["dn_bytes"] / (dn_ms * 1e-3) / 1e9
+        rec = recorded_traffic(name, "mixture_experts_layer_gemv_amd/csrc/expert_decode.hip")
+        roof = {"bound": "hbm", "achieved": round(gu_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gu_ach / HBM_PEAK_GBS, 4),
+                "traffic": rec["gate_up_traffic_bytes"] if rec else None,
+                "traffic_source": rec["profile"] if rec else None, "kernel": "gate_up_decode_kernel",
+                "algorithmic_bytes_per_launch": work["gu_bytes"], "avg_launch_ms": round(gu_ms, 5)}
+        layer_gbs = work["layer_bytes"] / (t["ms_per_step"] * 1e-3) / 1e9
+        kern = {"down_decode_kernel": {"avg_launch_ms": round(dn_ms, 5), "achieved_GBs": round(dn_ach, 1),
+                                       "frac": round(dn_ach / HBM_PEAK_GBS, 4),
+                                       "algorithmic_bytes_per_launch": work["dn_bytes"]},
+                "layer": {"bound": "hbm", "hbm_GBs": round(layer_gbs, 1), "hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
+                          "algorithmic_bytes": work["layer_bytes"]}}
+    else:
+        gu_ach = work["gu_flops"] / (gu_ms * 1e-3) / 1e12
+        dn_ach = work["dn_flops"] / (dn_ms * 1e-3) / 1e12
+        rec = recorded_traffic(name, "mixture_experts_layer_gemv_amd/csrc/expert_prefill.hip")
+        roof = {"bound": "mfma", "achieved": round(gu_ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(gu_ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": rec["gate_up_traffic_bytes"] if rec else None,
+                "traffic_source": rec["profile"] if rec else None,
+                "kernel": f"expert_prefill_kernel<true, {bm}>", "algorithmic_flops_per_launch": work["gu_flops"],
+                "algorithmic_bytes_per_launch": work["gu_bytes_prefill"], "avg_launch_ms": round(gu_ms, 5)}
+        layer_tf = work["layer_flops"] / (t["ms_per_step"] * 1e-3) / 1e12
+        kern = {f"expert_prefill_kernel<false, {bm}>": {"avg_launch_ms": round(dn_ms, 5),
+                                                        "achieved_TFLOPs": round(dn_ach, 1),
+                                                        "frac": round(dn_ach / MFMA_BF16_PEAK_TFLOPS, 4)},
+                "layer": {"bound": "mfma", "TFLOPs": round(layer_tf, 1),
+                          "mfma_frac": round(layer_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                          "algorithmic_flops": work["layer_flops"]}}
+        if s.d * s.f <= (1 << 23):
+            kern["layer"]["note"] = "expert matrices of 2^23 weights or fewer: launch- and latency-bound, not a roofline case"
+
+    res = {"T": T, "d": d, "f": f, "E": E, "k": k, "n_pad": s.n_pad, "description": s.description,
+           "value": round(T / (t["ms_per_step"] * 1e-3), 2), "unit": "tokens/s",
+           "non_pad_tokens_per_s": round((T - s.n_pad) / (t["ms_per_step"] * 1e-3), 2),
+           "ms_per_step": round(t["ms_per_step"], 5), "ms_median": round(t["ms_median"], 5),
+           "ms_min": round(t["ms_min"], 5), "touched_experts": work["touched"], "assignments": work["n_assign"],
+           "down_splits": splits, "expert_kernels": "streaming" if bm == 0 else f"tiled, {bm}-row tiles",
+           "roofline": roof, "kernels": kern}
+
+    if graph:
+        # the same forward captured once into a HIP graph and replayed (one launch per step)
+        ws = torch.empty(moe.workspace_bytes(T, d, f, E, k) + 256, dtype=torch.uint8, device=dev)
+        g = moe.Graph(wl.x, wl.wr, wl.wg, wl.wu, wl.wd, wl.sc, wl.pad, wl.out, T, d, f, E, k, router_bias=wl.bias,
+                      workspace=ws, workspace_bytes_=ws.numel())
+        try:
+            for _ in range(args.warmup):
+                g.launch(stream)
+            tg = timed_steps(lambda: g.launch(stream), args.steps, stream)
+        finally:
+            g.close()
+        res["graph"] = {k2: round(v, 5) for k2, v in tg.items()}
+        log(f"{name}: graph replay {tg['ms_per_step']:.4f} ms/step")
+
+    if cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(wl, cpu_seconds, host["oracle_threads"], name)
+        log(f"{name}: cpu oracle {res['cpu_baseline']['value']} tokens/s")
+    else:
+        res["cpu_baseline"] = None
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode",
-                    choices=["tiny", "decode", "batched_decode", "prefill", "skewed", "decode_tp8", "prefill_tp8"])
+    ap.add_argument("--workload", default="decode", choices=WORKLOADS)
+    ap.add_argument("--configs", default="metric", choices=["metric", "none"],
+                    help="metric: also time the other workloads the metric is defined on (reported under "
+                         "'configs'); none: only --workload (for profiler runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="target CPU time of the oracle baseline sample (0 = skip)")
+                    help="target CPU time of the headline workload's oracle baseline (0 = skip)")
+    ap.add_argument("--cpu-seconds-other", type=float, default=5.0,
+                    help="target CPU time of each other workload's oracle baseline (0 = skip)")
     ap.add_argument("--variant", default="gather", choices=["gather", "dense", "graph", "block"],
                     help="gather: moe_forward (the headline); dense: the one-hot-gated formulation; "
                          "graph: moe_forward replayed from a captured HIP graph; block: the MoE block with "
@@ -133,203 +376,88 @@ def main() -> int:
               "that path is not built.", file=sys.stderr, flush=True)
         return 2
 
-    import numpy as np
     import torch
 
     import mixture_experts_layer_gemv_amd as moe
-    import synth
 
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration, args.steps, args.warmup)
 
-    spec = synth.CONFIGS[args.workload]
-    T, d, f, E, k = spec.T, spec.d, spec.f, spec.E, spec.k
     torch.cuda.set_device(0)
-    dev = torch.device("cuda:0")
-
-    t0 = time.time()
-    inp = synth.make_inputs(spec)
-    log(f"generated {args.workload} inputs in {time.time() - t0:.1f}s")
-    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
-    bf = lambda a: to(a.view(np.int16)).view(torch.bfloat16)  # noqa: E731
-    x, wr, sc = bf(inp["x"]), to(inp["router_w"]), bf(inp["scales"])
-    wg, wu, wd = to(inp["w_gate"]), to(inp["w_up"]), to(inp["w_down"])
-    pad = None if inp["pad_mask"] is None else to(inp["pad_mask"])
-    bias = None if inp["router_bias"] is None else to(inp["router_bias"])
-    out = torch.empty((T, d), dtype=torch.float32, device=dev)
-    torch.cuda.synchronize()
-    log(f"inputs resident in HBM after {time.time() - t0:.1f}s")
-
-    stream = torch.cuda.current_stream()
-    counts_t = torch.empty(E, dtype=torch.int32, device=dev)
-
-    def step(dbg=None):
-        moe.moe_forward_ex(x, wr, wg, wu, wd, sc, pad, out, T, d, f, E, k, stream, router_bias=bias, dbg=dbg)
-
-    step(dbg={"counts": counts_t})  # allocates the library workspace (synchronising), outside timing
-    torch.cuda.synchronize()
-    counts = counts_t.cpu().tolist()
-    graph = None
-    if args.variant == "dense":
-        def step(dbg=None):  # noqa: F811
-            moe.moe_forward_dense(x, wr, wg, wu, wd, sc, pad, out, T, d, f, E, k, stream, router_bias=bias)
-    elif args.variant == "graph":
-        graph = moe.Graph(x, wr, wg, wu, wd, sc, pad, out, T, d, f, E, k, router_bias=bias)
-
-        def step(dbg=None):  # noqa: F811
-            graph.launch(stream)
-    elif args.variant == "block":
-        ones = torch.ones(d, dtype=torch.float32, device=dev)
-
-        def step(dbg=None):  # noqa: F811
-            moe.moe_block_forward(x, ones, ones, 1e-5, wr, wg, wu, wd, sc, pad, out, T, d, f, E, k, stream,
-                                  router_bias=bias)
-    step()
-    torch.cuda.synchronize()
-    gu_ms = dn_ms = None
-    if args.variant == "gather":
-        # ---- per-kernel durations (first, so that the GPU is at its steady clocks for the timed
-        #      steps after it): the same kernels through the stage entry points, with HIP events
-        #      recorded on the launch stream around the two expert kernels
-        tk = T * k
-        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-        wts = torch.empty((T, k), dtype=torch.float32, device=dev)
-        offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
-        perm = torch.empty(max(tk, 1), dtype=torch.int32, device=dev)
-        pos = torch.empty((T, k), dtype=torch.int32, device=dev)
-        h = torch.empty((tk, f), dtype=torch.float16, device=dev)
-        splits = moe.down_splits(T, d, f, E, k)
-        y = torch.empty((splits, tk, d), dtype=torch.float32, device=dev)
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-
-        def staged(e=None):
-            moe.moe_route(x, wr, bias, pad, ids, wts, T, d, E, k, stream)
-            moe.moe_dispatch(ids, pad, counts_t, offsets, perm, pos, T, E, k, stream)
-            if e:
-                e[0].record(stream)
-            moe.moe_gate_up(x, perm, offsets, wg, wu, sc, h, T, d, f, E, k, stream)
-            if e:
-                e[1].record(stream)
-                e[2].record(stream)
-            moe.moe_down(h, offsets, wd, sc, y, splits, T, d, f, E, k, stream)
-            if e:
-                e[3].record(stream)
-            moe.moe_combine(y, splits, pos, wts, pad, out, T, d, k, stream)
-
-        # from idle the GPU takes ~15 ms of work to reach its steady clocks: warm the staged
-        # passes up for at least 20 of them
-        for _ in range(max(20, args.warmup)):
-            staged()
-        torch.cuda.synchronize()
-        for i in range(args.steps):
-            staged(evs[i])
-        torch.cuda.synchronize()
-        gu_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-        dn_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
-        log(f"gate_up {gu_ms:.4f} ms, down {dn_ms:.4f} ms (splits={splits})")
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # ---- timed region: exactly K steps
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
-    log(f"{args.steps} steps: {ms_per_step:.4f} ms/step ({args.variant})")
+    host = host_info()
     if args.variant != "gather":
-        print(json.dumps({"metric": METRIC, "value": round(T / (ms_per_step * 1e-3), 2), "unit": "tokens/s",
+        wl = Inputs(args.workload)
+        s = wl.spec
+        stream = torch.cuda.current_stream()
+        if args.variant == "dense":
+            def step():
+                moe.moe_forward_dense(wl.x, wl.wr, wl.wg, wl.wu, wl.wd, wl.sc, wl.pad, wl.out, s.T, s.d, s.f, s.E, s.k,
+                                      stream, router_bias=wl.bias)
+        elif args.variant == "graph":
+            graph = moe.Graph(wl.x, wl.wr, wl.wg, wl.wu, wl.wd, wl.sc, wl.pad, wl.out, s.T, s.d, s.f, s.E, s.k,
+                              router_bias=wl.bias)
+
+            def step():
+                graph.launch(stream)
+        else:
+            ones = torch.ones(s.d, dtype=torch.float32, device="cuda:0")
+
+            def step():
+                moe.moe_block_forward(wl.x, ones, ones, 1e-5, wl.wr, wl.wg, wl.wu, wl.wd, wl.sc, wl.pad, wl.out,
+                                      s.T, s.d, s.f, s.E, s.k, stream, router_bias=wl.bias)
+        step()
+        for _ in range(args.warmup):
+            step()
+        t = timed_steps(step, args.steps, stream)
+        log(f"{args.steps} steps: {t['ms_per_step']:.4f} ms/step ({args.variant})")
+        print(json.dumps({"metric": METRIC, "value": round(s.T / (t["ms_per_step"] * 1e-3), 2), "unit": "tokens/s",
                           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-                          "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+                          "ms_per_step": round(t["ms_per_step"], 5), "ms_median": round(t["ms_median"], 5),
+                          "ms_min": round(t["ms_min"], 5), "higher_is_better": True, "scaling": "weak",
                           "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "variant": args.variant,
-                          "config": {"workload": f"{args.workload}: {spec.description}", "T": T, "d": d, "f": f,
-                                     "E": E, "k": k, "n_pad": spec.n_pad}}), flush=True)
+                          "config": {"workload": f"{args.workload}: {s.description}", "T": s.T, "d": s.d, "f": s.f,
+                                     "E": s.E, "k": s.k, "n_pad": s.n_pad}}), flush=True)
         return 0
 
-    work = algorithmic_work(spec, counts)
-    bm = moe.expert_kernels(T, d, f, E, k)  # 0: streaming kernels, else tiled with bm-row tiles
-    streaming = bm == 0
-    if streaming:
-        gu_ach = work["gu_bytes"] / (gu_ms * 1e-3) / 1e9
-        dn_ach = work["dn_bytes"] / (dn_ms * 1e-3) / 1e9
-        rec = recorded_traffic(args.workload, "mixture_experts_layer_gemv_amd/csrc/expert_decode.hip")
-        roof = {"bound": "hbm", "achieved": round(gu_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gu_ach / HBM_PEAK_GBS, 4),
-                "traffic": rec["gate_up_traffic_bytes"] if rec else None,
-                "traffic_source": rec["profile"] if rec else None, "kernel": "gate_up_decode_kernel",
-                "algorithmic_bytes_per_launch": work["gu_bytes"], "avg_launch_ms": round(gu_ms, 5)}
-        kern = {"down_decode_kernel": {"avg_launch_ms": round(dn_ms, 5), "achieved_GBs": round(dn_ach, 1),
-                                       "frac": round(dn_ach / HBM_PEAK_GBS, 4),
-                                       "algorithmic_bytes_per_launch": work["dn_bytes"]},
-                "layer": {"hbm_GBs": round(work["layer_bytes"] / (ms_per_step * 1e-3) / 1e9, 1),
-                          "hbm_frac": round(work["layer_bytes"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                          "algorithmic_bytes": work["layer_bytes"]}}
-    else:
-        gu_ach = work["gu_flops"] / (gu_ms * 1e-3) / 1e12
-        dn_ach = work["dn_flops"] / (dn_ms * 1e-3) / 1e12
-        rec = recorded_traffic(args.workload, "mixture_experts_layer_gemv_amd/csrc/expert_prefill.hip")
-        roof = {"bound": "mfma", "achieved": round(gu_ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(gu_ach / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": rec["gate_up_traffic_bytes"] if rec else None,
-                "traffic_source": rec["profile"] if rec else None,
-                "kernel": f"expert_prefill_kernel<true, {bm}>", "algorithmic_flops_per_launch": work["gu_flops"],
-                "algorithmic_bytes_per_launch": work["gu_bytes_prefill"], "avg_launch_ms": round(gu_ms, 5)}
-        layer_tf = work["layer_flops"] / (ms_per_step * 1e-3) / 1e12
-        kern = {f"expert_prefill_kernel<false, {bm}>": {"avg_launch_ms": round(dn_ms, 5), "achieved_TFLOPs": round(dn_ach, 1),
-                                                 "frac": round(dn_ach / MFMA_BF16_PEAK_TFLOPS, 4)},
-                "layer": {"TFLOPs": round(layer_tf, 1), "mfma_frac": round(layer_tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                          "algorithmic_flops": work["layer_flops"]}}
-
-    # ---- CPU baseline: the oracle as it stands, on a bounded sample of the same workload
-    cpu = None
-    if args.cpu_seconds > 0:
-        import oracle
-
-        try:
-            cores = len(os.sched_getaffinity(0))
-        except AttributeError:
-            cores = os.cpu_count() or 1
-        cores = max(1, min(cores, 16))
-        rows = np.arange(T) if T <= 16 else np.random.default_rng(0).choice(T, 16, replace=False)
-        reps, tok, t_start = 0, 0, time.time()
-        while True:
-            oracle.forward_inputs(inp, k=k, nthreads=cores, rows=rows)
-            reps += 1
-            tok += len(rows)
-            if time.time() - t_start >= args.cpu_seconds or reps >= 1000:
-                break
-        el = time.time() - t_start
-        cpu = {"value": round(tok / el, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-               "sample": f"{reps} oracle forward(s) of {len(rows)} token rows of the {args.workload} workload "
-                         f"({el:.1f} s wall, fp32, {cores} threads)"}
-        log(f"cpu oracle: {cpu['value']} tokens/s")
+    head = measure(args.workload, args, host, args.cpu_seconds, graph=args.workload in ("tiny", "decode"))
+    others = {}
+    if args.configs == "metric":
+        # the Grok-shape workloads share one weight set: run them together, the tiny layer last
+        for name in sorted(METRIC_WORKLOADS, key=lambda n: n == "tiny"):
+            if name != args.workload:
+                others[name] = measure(name, args, host, args.cpu_seconds_other, graph=name in ("tiny", "decode"))
 
     line = {
         "metric": METRIC,
-        "value": round(T / (ms_per_step * 1e-3), 2),
+        "value": head["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": head["ms_per_step"],
+        "ms_median": head["ms_median"],
+        "ms_min": head["ms_min"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: {spec.description}", "T": T, "d": d, "f": f, "E": E, "k": k,
-                   "n_pad": spec.n_pad, "weights": "int8 + bf16 per-output-channel scales",
-                   "touched_experts": work["touched"], "assignments": work["n_assign"], "down_splits": splits,
-                   "parallelism": "single GPU"},
-        "roofline": roof,
-        "kernels": kern,
-        "cpu_baseline": cpu,
+        "config": {"workload": f"{args.workload}: {head['description']}", "T": head["T"], "d": head["d"],
+                   "f": head["f"], "E": head["E"], "k": head["k"], "n_pad": head["n_pad"],
+                   "weights": "int8 + bf16 per-output-channel scales", "touched_experts": head["touched_experts"],
+                   "assignments": head["assignments"], "down_splits": head["down_splits"],
+                   "expert_kernels": head["expert_kernels"], "parallelism": "single GPU"},
+        "non_pad_tokens_per_s": head["non_pad_tokens_per_s"],
+        "roofline": head["roofline"],
+        "kernels": head["kernels"],
+        "cpu_baseline": head["cpu_baseline"],
+        "host": host,
     }
+    if "graph" in head:
+        line["graph"] = head["graph"]
+    if others:
+        line["configs"] = {n: {k2: v for k2, v in r.items() if k2 not in ("description",)} | {"workload": r["description"]}
+                           for n, r in others.items()}
     print(json.dumps(line), flush=True)
     return 0
 
