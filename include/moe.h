@@ -157,6 +157,22 @@ int moe_expert_kernels(int T, int d, int f, int E, int k);
 int moe_combine(const float* y, int splits, const int32_t* pos, const float* topk_w,
                 const uint8_t* pad_mask, float* out, int T, int d, int k, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+   loops, harnesses that forbid hipMalloc): moe_forward_ex without workspace or dbg arguments,
+   whose scratch (the routing, dispatch, H and Y arrays) is a fixed array of
+   MOE_NOALLOC_SCRATCH_BYTES in device memory that the library defines, one per device, held
+   until the process ends. The call allocates and frees nothing (no hipMalloc or hipFree, no
+   allocating library routine); its first call on a device looks up that device's copy of the
+   array. Shapes whose workspace (moe_workspace_bytes) exceeds MOE_NOALLOC_SCRATCH_BYTES are
+   rejected with MOE_ERR_UNSUPPORTED before anything is enqueued: 64 MiB hold the Grok-1 shape
+   (d = 6144, f = 32768) up to 204 tokens. Every call on a device shares that device's
+   array: calls that overlap in time on one device (other streams, other threads) race.
+   Results equal moe_forward_ex's bit for bit; errors as moe_forward_ex. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_forward_noalloc(const void* x, const float* router_w, const int8_t* w_gate, const int8_t* w_up,
+                        const int8_t* w_down, const void* scales, const uint8_t* pad_mask, float* out,
+                        int T, int d, int f, int E, int k, void* stream, const float* router_bias);
+
 /* The dense one-hot-gated formulation the sources describe for their own implementation
    (Guide section 3, MoE step 4 and the warning under it): every one of the E experts runs
    on every real token and out[t] = sum over e (in order) of gate[t][e] * y_e(t), where

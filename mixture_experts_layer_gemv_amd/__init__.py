@@ -33,6 +33,7 @@ SIGNATURES = {
     "moe_expert_kernels": ([_i32] * 5, _i32),
     "moe_combine": ([_vp] + [_i32] + [_vp] * 4 + [_i32] * 3 + [_vp], _i32),
     "moe_workspace_bytes": ([_i32] * 5, _sz),
+    "moe_forward_noalloc": ([_vp] * 8 + [_i32] * 5 + [_vp, _vp], _i32),
     "moe_forward_dense": ([_vp] * 8 + [_i32] * 5 + [_vp, _vp, _vp, _sz], _i32),
     "moe_workspace_bytes_dense": ([_i32] * 5, _sz),
     "moe_block_forward": ([_vp, _vp, _vp, ctypes.c_float] + [_vp] * 7 + [_i32] * 5 + [_vp, _vp, _vp, _sz, _vp], _i32),
@@ -137,6 +138,16 @@ def moe_forward_ex(x, router_w, w_gate, w_up, w_down, scales, pad_mask, out, T, 
                                 _ptr(pad_mask), _ptr(out), T, d, f, E, k, _stream(stream), _ptr(router_bias),
                                 _ptr(workspace), workspace_bytes_,
                                 ctypes.byref(dbg_struct) if dbg_struct is not None else None))
+
+
+def moe_forward_noalloc(x, router_w, w_gate, w_up, w_down, scales, pad_mask, out, T, d, f, E, k, stream=None,
+                        router_bias=None) -> None:
+    """moe_forward_ex whose scratch is the library's fixed per-device array (allocates nothing)."""
+    _check(lib().moe_forward_noalloc(_ptr(x), _ptr(router_w), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(scales),
+                                     _ptr(pad_mask), _ptr(out), T, d, f, E, k, _stream(stream), _ptr(router_bias)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def moe_forward_dense(x, router_w, w_gate, w_up, w_down, scales, pad_mask, out, T, d, f, E, k, stream=None,

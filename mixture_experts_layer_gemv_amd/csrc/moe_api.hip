@@ -128,6 +128,29 @@ size_t block_sumsq_bytes(int T, int d) {
 }
 size_t block_prefix_bytes(int T, int d) { return round_up((size_t)T * d * 2, 256) + block_sumsq_bytes(T, d); }
 
+// Scratch of moe_forward_noalloc: a fixed array in device memory (one copy per device, held
+// until the process ends). Host code never passes `scratch` itself to a kernel (on the host the
+// name stands for a host-side shadow, not the device address): its device address is looked up
+// once per device with hipGetSymbolAddress and kept in g_scratch.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mutex;
+std::vector<void*> g_scratch;
+
+int scratch_address(char** out) {
+  int dev = 0;
+  MOE_HIP(hipGetDevice(&dev), "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if ((int)g_scratch.size() <= dev) g_scratch.resize(dev + 1, nullptr);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    MOE_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch[dev] = p;
+  }
+  *out = static_cast<char*>(g_scratch[dev]);
+  return MOE_OK;
+}
+
 struct DeviceWorkspace {
   void* ptr = nullptr;
   size_t bytes = 0;
@@ -314,6 +337,24 @@ int moe_forward_ex(const void* x, const float* router_w, const int8_t* w_gate, c
       if (c.dst) MOE_HIP(hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyDeviceToDevice, s), "debug copy");
   }
   return MOE_OK;
+}
+
+int moe_forward_noalloc(const void* x, const float* router_w, const int8_t* w_gate, const int8_t* w_up,
+                        const int8_t* w_down, const void* scales, const uint8_t* pad_mask, float* out, int T, int d,
+                        int f, int E, int k, void* stream, const float* router_bias) {
+  MOE_TRY(check_layer_args(x, router_w, w_gate, w_up, w_down, scales, out, T, d, f, E, k));
+  if (router_bias && !aligned(router_bias, 4)) return fail(MOE_ERR_INVALID, "router_bias is not 4-byte aligned");
+  if (T == 0) return MOE_OK;
+  const size_t need = make_layout(T, d, f, E, k).total;
+  if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_forward_noalloc: this shape needs " + std::to_string(need) +
+                                         " bytes of scratch, above its fixed " +
+                                         std::to_string((size_t)MOE_NOALLOC_SCRATCH_BYTES) +
+                                         " bytes (use moe_forward_ex with a workspace)");
+  char* ws = nullptr;
+  MOE_TRY(scratch_address(&ws));
+  return moe_forward_ex(x, router_w, w_gate, w_up, w_down, scales, pad_mask, out, T, d, f, E, k, stream, router_bias,
+                        ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, nullptr);
 }
 
 size_t moe_workspace_bytes_dense(int T, int d, int f, int E, int k) {
