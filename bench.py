@@ -83,6 +83,11 @@ def algorithmic_work(spec, counts):
                 gu_bytes_prefill=gu_bytes_prefill, gu_flops=gu_flops, dn_flops=dn_flops, layer_flops=layer_flops)
 
 
+def prefill_kernel_name(gate_up: bool, bm: int) -> str:
+    """The tiled kernel the library launches for bm-row tiles (256: the 4-wavefront kernel)."""
+    return f"expert_wide_kernel<{str(gate_up).lower()}>" if bm == 256 else f"expert_prefill_kernel<{str(gate_up).lower()}, {bm}>"
+
+
 def recorded_traffic(workload: str, source: str):
     """HBM traffic of the gate/up kernel as measured by rocprofv3 FETCH_SIZE / WRITE_SIZE
     (scaled by the copy calibration) and recorded in profiles/, or None when no record
@@ -305,10 +310,10 @@ def measure(name: str, args, host: dict, cpu_seconds: float, graph: bool) -> dic
                 "frac": round(gu_ach / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": rec["gate_up_traffic_bytes"] if rec else None,
                 "traffic_source": rec["profile"] if rec else None,
-                "kernel": f"expert_prefill_kernel<true, {bm}>", "algorithmic_flops_per_launch": work["gu_flops"],
+                "kernel": prefill_kernel_name(True, bm), "algorithmic_flops_per_launch": work["gu_flops"],
                 "algorithmic_bytes_per_launch": work["gu_bytes_prefill"], "avg_launch_ms": round(gu_ms, 5)}
         layer_tf = work["layer_flops"] / (t["ms_per_step"] * 1e-3) / 1e12
-        kern = {f"expert_prefill_kernel<false, {bm}>": {"avg_launch_ms": round(dn_ms, 5),
+        kern = {prefill_kernel_name(False, bm): {"avg_launch_ms": round(dn_ms, 5),
                                                         "achieved_TFLOPs": round(dn_ach, 1),
                                                         "frac": round(dn_ach / MFMA_BF16_PEAK_TFLOPS, 4)},
                 "layer": {"bound": "mfma", "TFLOPs": round(layer_tf, 1),
