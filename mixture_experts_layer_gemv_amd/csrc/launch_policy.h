@@ -45,6 +45,16 @@ inline int down_splits(int T, int d, int f, int E, int k) {
     const long tiles = (rows + 255) / 256 + std::min<long>(E, rows) / 2;
     return rows <= 8192 && tiles * (d / 256) <= 256 && (f / 128) % 4 == 0 ? 4 : 2;
   }
+  if (!streaming_experts(T, d, f)) {
+    // small expert matrices in the tiled kernels: with few live tiles (about one row tile per
+    // reachable expert x d / 256 column tiles) each workgroup would run the whole contraction
+    // alone, one dependent slice after another; split it into up to 16 parts of at least 128
+    // rows (two slices) while the parts still fit in one round of workgroups
+    const long tiles = std::min<long>(E, (long)T * k) * (d / 256);
+    int s = 1;
+    while (s < 16 && tiles * 2 * s <= 256 && f / (2 * s) >= 128 && (f / 128) % (2 * s) == 0) s *= 2;
+    return s;
+  }
   const long slabs = (long)(d / 256) * std::min<long>(E, (long)T * k);
   const long target = T <= 16 ? 768 : 512;
   int s = 1;

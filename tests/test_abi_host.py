@@ -89,10 +89,13 @@ def test_workspace_size_and_split_policy():
     # decode shapes split the down projection's contraction to fill the chip
     assert moe.down_splits(8, 6144, 32768, 8, 2) == 4
     assert moe.down_splits(64, 6144, 32768, 8, 2) == 4
-    assert moe.down_splits(64, 256, 512, 8, 2) == 1
+    # small matrices (the tiled kernels at any T): parts of >= 128 rows while one round of
+    # workgroups holds them (the tiny layer: 8 row tiles x 1 column tile -> 4 parts)
+    assert moe.down_splits(64, 256, 512, 8, 2) == 4
+    assert moe.down_splits(8, 1536, 2048, 8, 2) == 4
+    assert moe.down_splits(100, 6144, 1024, 8, 2) == 1
     # narrow f (one GPU's share of 8-way tensor parallelism): split until the chip is filled
     assert moe.down_splits(8, 6144, 4096, 8, 2) == 4
-    assert moe.down_splits(8, 1536, 2048, 8, 2) == 2
     assert moe.down_splits(64, 6144, 4096, 8, 2) == 4
     assert moe.down_splits(8192, 6144, 4096, 8, 2) == 1
     # the policy counts the experts a batch can reach, min(E, T * k)
@@ -110,8 +113,9 @@ def test_workspace_size_and_split_policy():
     assert moe.down_splits(4097, 256, 8192, 8, 2) == 2
     assert moe.down_splits(200, 256, 8448, 8, 2) == 2  # f / 128 = 66: quarters are not whole 128-row steps
     assert moe.down_splits(200, 256, 4096, 8, 2) == 1
-    # up to 160 tokens the streaming kernels run, with the small-batch policy
-    assert moe.down_splits(160, 256, 8192, 8, 2) == 8
+    # up to 160 tokens matrices of at most 2^23 weights take the tiled kernels, split in parts of
+    # >= 128 rows while one round of workgroups holds them (8 row tiles x 1 column tile: 16 parts)
+    assert moe.down_splits(160, 256, 8192, 8, 2) == 16
     # the gate/up split's partial sums are part of the decode workspace at narrow f
     assert moe.workspace_bytes(8, 6144, 4096, 8, 2) >= 2 * 4 * 16 * 4096 * 4
     assert moe.workspace_bytes(8, 6144, 32768, 8, 2) < 16 * 32768 * 2 + 8 * 16 * 6144 * 4 + (1 << 20)
