@@ -482,10 +482,14 @@ def test_layer_at_the_assignment_limit():
 # keeps fewer or all on the device (the combine reads its choice). 20 live workgroups
 # under-fill the chip: 2 parts; 16 m-tiles x 16 column tiles = exactly one round of 256: 1
 # part; 600 rows in 128-row tiles x 2 column tiles: 4 parts; all rows padded: 1 part.
+# 800 and 1500 tokens with f = 8448 (f / 256 odd): launched with 2 parts of 66 slices, which the
+# 256-row kernel runs as 16 trips of 4 slices and a 2-slice remainder (1 part: 132 slices)
 @pytest.mark.parametrize("kw", [dict(T=2048, d=256, f=8192, E=8, k=2, n_pad=17),
                                 dict(T=4096, d=4096, f=8192, E=1, k=1),
                                 dict(T=600, d=512, f=8192, n_pad=3),
-                                dict(T=300, d=256, f=8192, n_pad=300)])
+                                dict(T=300, d=256, f=8192, n_pad=300),
+                                dict(T=800, d=256, f=8448, n_pad=9),
+                                dict(T=1500, d=512, f=8448, bias=(2.0, 1.0, 0.5, 0, 0, 0, 0, -1.0))])
 def test_prefill_down_parts_chosen_on_device(kw):
     inp, d = small_case("parts", **kw)
     if kw.get("n_pad") == kw["T"]:  # nothing to compare against: +0.0 everywhere
@@ -761,3 +765,25 @@ def test_expert_relabelling_commutes(kw):
     err = float(np.abs(b - a).max() / rms(a))
     print(f"relabelling {kw}: bit-exact={bool(np.array_equal(a, b))} max|err|/rms={err:.2e}", flush=True)
     assert err <= 1e-5
+
+
+@pytest.mark.parametrize("splits", [1, 2])
+def test_down_stage_odd_slab_count(splits):
+    # f = 8448 (f / 256 odd) in 256-row tiles: with 2 parts each part is 66 slices, 16 trips of
+    # the 4-slice loop and the 2-slice remainder; with 1 part 132 slices (no remainder)
+    T, dd, f = 800, 256, 8448
+    inp, d = small_case("odd_slabs", T=T, d=dd, f=f, n_pad=5)
+    assert moe.expert_kernels(T, dd, f, 8, 2) == 256
+    r = oracle.route(inp["x"], inp["router_w"], inp["router_bias"], inp["pad_mask"], 2)
+    disp = oracle.dispatch(r["ids"], inp["pad_mask"], 8)
+    h16 = fp16_from_normal(77, (T * 2, f))
+    offsets = torch.from_numpy(disp["offsets"]).cuda()
+    y = torch.full((splits, T * 2, dd), float("nan"), dtype=torch.float32, device="cuda")
+    moe.moe_down(torch.from_numpy(h16).cuda(), offsets, d["w_down"], d["scales"], y, splits, T, dd, f, 8, 2)
+    torch.cuda.synchronize()
+    seg, ntiles = segment_rows(disp["offsets"], 8, 256, all_up_to=0)
+    for e, rows in seg.items():
+        yg = y[:, torch.tensor(rows, device="cuda")].cpu().numpy().astype(np.float64).sum(0)
+        yref = oracle.expert_down(np.ascontiguousarray(h16[rows].astype(np.float32)), inp["w_down"], inp["scales"], e)
+        assert np.max(np.abs(yg - yref)) <= 1e-4 * rms(yref), e
+    print(f"down f={f} splits={splits}: {sum(len(r) for r in seg.values())} rows over {ntiles} tiles", flush=True)
