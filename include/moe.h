@@ -93,7 +93,10 @@ int moe_forward(const void* x, const float* router_w, const int8_t* w_gate, cons
 /* Same as moe_forward, plus:
    router_bias  fp32 [E] added to the logits before the softmax, or NULL;
    workspace    caller-owned device buffer of at least moe_workspace_bytes(T, d, f, E, k)
-                bytes (256-byte aligned), or NULL to use the library workspace;
+                bytes (256-byte aligned), or NULL to use the library workspace (on the
+                one-launch path, see moe_one_launch, it also holds that kernel's control
+                block, which the call zeroes with a small kernel first; any prior contents
+                are fine);
    dbg          optional copies of the routing and dispatch arrays, or NULL. */
 int moe_forward_ex(const void* x, const float* router_w, const int8_t* w_gate, const int8_t* w_up,
                    const int8_t* w_down, const void* scales, const uint8_t* pad_mask, float* out,
@@ -151,6 +154,16 @@ int moe_down_splits(int T, int d, int f, int E, int k);
    average) or 256. -1 for a shape the library rejects (moe_last_error() says why). Host only:
    no device call, no allocation. */
 int moe_expert_kernels(int T, int d, int f, int E, int k);
+
+/* The one-launch layer, an alternative to the launch-per-stage sequence for small batches
+   (T <= 64, E = 8, expert matrices above 2^23 weights; not T <= 4 when the gate/up
+   contraction is whole): routing, dispatch, both expert matrices and the combine run as work
+   items of one kernel, with the same arithmetic in the same order, so the result is the same
+   bits. It is slower on MI355X than one launch per stage (waiting items hold whole SIMDs), so
+   moe_forward, moe_forward_ex, moe_forward_noalloc and moe_graph_create take it only when the
+   environment variable MOE_ONE_LAUNCH is "1" at the call. Returns 1 if they would take it for
+   this shape now, 0 if not, -1 for a shape the library rejects. Host only. */
+int moe_one_launch(int T, int d, int f, int E, int k);
 
 /* Step 4: out[t] = sum over j of topk_w[t][j] * (sum over parts s of y[s][pos[t][j]]),
    parts in order, slots in order, fp32; +0.0 rows for padded tokens. */

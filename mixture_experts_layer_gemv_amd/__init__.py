@@ -31,6 +31,7 @@ SIGNATURES = {
     "moe_down": ([_vp] * 5 + [_i32] * 6 + [_vp], _i32),
     "moe_down_splits": ([_i32] * 5, _i32),
     "moe_expert_kernels": ([_i32] * 5, _i32),
+    "moe_one_launch": ([_i32] * 5, _i32),
     "moe_combine": ([_vp] + [_i32] + [_vp] * 4 + [_i32] * 3 + [_vp], _i32),
     "moe_workspace_bytes": ([_i32] * 5, _sz),
     "moe_forward_noalloc": ([_vp] * 8 + [_i32] * 5 + [_vp, _vp], _i32),
@@ -118,6 +119,11 @@ def down_splits(T: int, d: int, f: int, E: int, k: int) -> int:
 def expert_kernels(T: int, d: int, f: int, E: int, k: int) -> int:
     """0: the streaming expert kernels run; 128 / 256: the tiled ones, with tiles of that many rows."""
     return lib().moe_expert_kernels(T, d, f, E, k)
+
+
+def one_launch(T: int, d: int, f: int, E: int, k: int) -> int:
+    """1 if the forward runs this shape as one kernel launch, 0 if one launch per stage."""
+    return lib().moe_one_launch(T, d, f, E, k)
 
 
 def release_workspace() -> None:

@@ -6,7 +6,7 @@
 // slots with pos < 0) contribute nothing; padded rows are +0.0.
 // grid (T, ceil(d / (4 * block))), block 64 (T <= 160) or 256: each thread writes 4 adjacent
 // columns.
-#include "device_common.h"
+#include "combine_common.h"
 #include "kernels.h"
 
 namespace moe {
@@ -22,17 +22,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   if (c >= d) return;
   if (splits_dev) splits = *splits_dev;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (pad_mask == nullptr || pad_mask[t] != 0) {
-    for (int j = 0; j < k; ++j) {
-      const int p = pos[(size_t)t * k + j];
-      if (p < 0) continue;
-      const float wj = topk_w[(size_t)t * k + j];
-      const float* src = Y + (size_t)p * d + c;
-      f32x4 y = *reinterpret_cast<const f32x4*>(src);
-      for (int s = 1; s < splits; ++s) y += *reinterpret_cast<const f32x4*>(src + (size_t)s * part_stride);
-      acc += wj * y;
-    }
-  }
+  if (pad_mask == nullptr || pad_mask[t] != 0) acc = gather_combine(Y, splits, part_stride, pos, topk_w, t, c, d, k);
   *reinterpret_cast<f32x4*>(out + (size_t)t * d + c) = acc;
 }
 
@@ -59,22 +49,6 @@ __device__ __forceinline__ float chunk_sumsq(const f32x4& m, float* s_red) {
   if (lane == 0) s_red[wave] = v;
   __syncthreads();
   return s_red[0] + s_red[1] + s_red[2] + s_red[3];
-}
-
-__device__ __forceinline__ f32x4 gather_combine(const float* __restrict__ Y, int splits, size_t part_stride,
-                                                const int32_t* __restrict__ pos,
-                                                const float* __restrict__ topk_w, int t, int c, int d, int k) {
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const int p = pos[(size_t)t * k + j];
-    if (p < 0) continue;
-    const float wj = topk_w[(size_t)t * k + j];
-    const float* src = Y + (size_t)p * d + c;
-    f32x4 y = *reinterpret_cast<const f32x4*>(src);
-    for (int s = 1; s < splits; ++s) y += *reinterpret_cast<const f32x4*>(src + (size_t)s * part_stride);
-    acc += wj * y;
-  }
-  return acc;
 }
 
 __device__ __forceinline__ f32x4 residual_postnorm(const f32x4& m, float r, const float* __restrict__ norm_post,

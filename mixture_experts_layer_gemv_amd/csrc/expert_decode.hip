@@ -11,120 +11,17 @@
 // split). For gate/up a workgroup holds two wavefronts, one per matrix, on the same slab;
 // they meet in LDS for the GeGLU epilogue, or, when the contraction is split, write fp32
 // partial sums that geglu_finish_kernel adds in part order before the same epilogue; at
-// T <= 4 one wavefront streams both matrices (gate_up_fused_decode_kernel). Lane l takes the 16 adjacent columns
-// n0 + 16 (l % 16) .. + 15 and, per 32-deep step, the rows k0 + 8 (l / 16) .. + 7: eight
-// 16-byte loads, so each row segment a wavefront instruction touches is 256 contiguous
-// bytes. Byte j of those eight rows is exactly the B operand of one 16x16x32 MFMA (column
-// j of the lane's 16 columns); the matching A operand (8 bf16/fp16 activations of the same
-// k-group) is one 16-byte load. The k order inside an MFMA is the same permutation for A
-// and B, so it does not change D. The int8 -> bf16 / fp16 conversion is exact (one
-// sign-extending byte convert plus half a pack per element); scales are applied in fp32
-// after the contraction. Loads run kStages - 1 steps ahead of the MFMAs (register ring).
+// T <= 4 one wavefront streams both matrices (gate_up_fused_decode_kernel). The inner loop
+// (lane layout, MFMA operands, load ring) is stream_slab in stream_common.h.
 //
 // Rows: an expert's segment of the dispatch has M rows (M <= T). A pass covers MT
 // 16-row MFMA tiles (MT = 1 when T <= 16 (gate/up with the whole contraction: T <= 8), 2
 // when T <= 64, else 3, the most the registers hold); longer segments take further passes
 // over the weights.
-#include "device_common.h"
 #include "kernels.h"
+#include "stream_common.h"
 
 namespace moe {
-
-namespace {
-constexpr int kStep = 32;    // contraction rows per MFMA step
-// Cache policy of the weight loads: non-temporal (each weight byte is read once).
-constexpr int kWeightLoadPolicy = 2;
-// Buffer resource word 3 for raw byte buffers on gfx9-family parts.
-constexpr int kBufferFlags = 0x00020000;
-}  // namespace
-
-// Shape of the streaming kernels: kNcol adjacent columns per lane (16-byte loads, so a
-// wavefront instruction reads 256-byte row segments and a wavefront owns a 256-column
-// slab); the depth of the load ring is a template parameter of each kernel.
-constexpr int kNcol = 16;
-constexpr int kSlab = 16 * kNcol;  // columns per wavefront
-
-__device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-
-template <int J, typename V, int NW>
-__device__ __forceinline__ V col_operand(const uint32_t (&w)[8][NW]) {
-  uint32_t s[8];
-#pragma unroll
-  for (int r = 0; r < 8; ++r) s[r] = w[r][J >> 2];
-  if constexpr (__is_same(V, bf16x8))
-    return rows_to_bf16<J & 3>(s);
-  else
-    return rows_to_f16<J & 3>(s);
-}
-
-template <int NW>
-__device__ __forceinline__ void load_row(uint32_t (&dst)[NW], __amdgpu_buffer_rsrc_t wr, uint32_t voff, uint32_t soff) {
-  if constexpr (NW == 2) {
-    auto v = __builtin_amdgcn_raw_buffer_load_b64(wr, voff, soff, kWeightLoadPolicy);
-    dst[0] = v[0], dst[1] = v[1];
-  } else {
-    auto v = __builtin_amdgcn_raw_buffer_load_b128(wr, voff, soff, kWeightLoadPolicy);
-    dst[0] = v[0], dst[1] = v[1], dst[2] = v[2], dst[3] = v[3];
-  }
-}
-
-// acc[mt][j] += A rows (tile mt) x column j of the lane's NCOL, over `steps` 32-deep steps.
-// wr: buffer resource of this expert's matrix; voff: byte offset of this lane's first
-// weight (row 8 kg, column n0); row r of step s is at voff + (32 s + r) * ld, with the
-// uniform part in the scalar offset, so all eight row loads share one address register.
-// a[mt]: this lane's first activation of tile mt (row cl of the tile, k 8 kg). Rows past
-// the segment end point at a live row: MFMA rows are independent, so their results are
-// simply not stored. The steady-state loop has no branches, so the loads of the next
-// kStages - 1 steps stay in flight across the MFMAs; a short unrolled tail finishes.
-template <typename Frag, int MT, int kStages>
-__device__ __forceinline__ void stream_slab(__amdgpu_buffer_rsrc_t wr, uint32_t voff, uint32_t ld, int steps,
-                                            const uint16_t* const (&a)[MT], f32x4 (&acc)[MT][kNcol]) {
-  constexpr int NW = kNcol / 4;
-  uint32_t b[kStages][8][NW];
-  u32x4 av[kStages][MT];
-  auto load = [&](int s, int step) {
-    const uint32_t base = (uint32_t)step * kStep * ld;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) load_row<NW>(b[s][r], wr, voff, base + r * ld);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) av[s][mt] = load16(a[mt] + step * kStep);
-  };
-  auto compute = [&](int s) {
-    Frag af[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) af[mt] = __builtin_bit_cast(Frag, av[s][mt]);
-#define MOE_DEC_COL(J)                                                          \
-  if constexpr ((J) < kNcol) {                                                  \
-    Frag bfr = col_operand<(J), Frag, NW>(b[s]);                                \
-    _Pragma("unroll") for (int mt = 0; mt < MT; ++mt)                           \
-        acc[mt][(J)] = Mfma<Frag>::run(af[mt], bfr, acc[mt][(J)]);              \
-  }
-    MOE_DEC_COL(0) MOE_DEC_COL(1) MOE_DEC_COL(2) MOE_DEC_COL(3)
-    MOE_DEC_COL(4) MOE_DEC_COL(5) MOE_DEC_COL(6) MOE_DEC_COL(7)
-    MOE_DEC_COL(8) MOE_DEC_COL(9) MOE_DEC_COL(10) MOE_DEC_COL(11)
-    MOE_DEC_COL(12) MOE_DEC_COL(13) MOE_DEC_COL(14) MOE_DEC_COL(15)
-#undef MOE_DEC_COL
-  };
-
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < steps) load(s, s);
-  int st = 0;
-  for (; st + 2 * kStages - 1 <= steps; st += kStages) {
-#pragma unroll
-    for (int s = 0; s < kStages; ++s) {
-      load((s + kStages - 1) % kStages, st + s + kStages - 1);
-      compute(s);
-    }
-  }
-#pragma unroll
-  for (int s = 0; s < 2 * kStages - 1; ++s) {
-    if (st + s < steps) {
-      if (st + s + kStages - 1 < steps) load((s + kStages - 1) % kStages, st + s + kStages - 1);
-      compute(s % kStages);
-    }
-  }
-}
 
 // The same stream over two matrices at once (gate and up of one slab): both rings share
 // the activation loads; accg / accu take the two products.
@@ -198,21 +95,6 @@ __device__ __forceinline__ bool skip_by_segment(const int32_t* __restrict__ offs
   if constexpr (kOnly == 0) return false;
   const int m = max_segment(offsets, E);
   return kOnly == 1 ? m > 32 : m <= 32;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const int8_t* base, size_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(base), (short)0, (int)bytes, kBufferFlags);
-}
-
-template <int N>
-__device__ __forceinline__ void load_scales(const uint16_t* p, float (&s)[N]) {
-#pragma unroll
-  for (int q = 0; q < N / 8; ++q) {
-    u32x4 v = load16(p + 8 * q);
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) s[8 * q + j] = bf16_bits_to_float((w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-  }
 }
 
 // ------------------------------------------------------------------------------------
@@ -384,25 +266,7 @@ __global__ __launch_bounds__(256) void geglu_finish_kernel(const float* __restri
   const uint16_t* sc = scales + (size_t)e * (2 * (size_t)f + d);
   const size_t plane = (size_t)rows_cap * f;
   const int n = 2048 * blockIdx.y + 8 * threadIdx.x;
-  if (n < f) {
-    f32x4 g[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    f32x4 u[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    for (int p = 0; p < parts; ++p) {
-      const f32x4* gp = reinterpret_cast<const f32x4*>(P + (2 * p) * plane + (size_t)r * f + n);
-      const f32x4* up = reinterpret_cast<const f32x4*>(P + (2 * p + 1) * plane + (size_t)r * f + n);
-      g[0] += gp[0], g[1] += gp[1];
-      u[0] += up[0], u[1] += up[1];
-    }
-    float sg[8], su[8];
-    load_scales<8>(sc + n, sg);
-    load_scales<8>(sc + f + n, su);
-    uint32_t packed[4];
-#pragma unroll
-    for (int j = 0; j < 8; j += 2)
-      packed[j >> 1] = pack_f16_rne(gelu_tanh(g[j >> 2][j & 3] * sg[j]) * (u[j >> 2][j & 3] * su[j]),
-                                    gelu_tanh(g[j >> 2][(j & 3) + 1] * sg[j + 1]) * (u[j >> 2][(j & 3) + 1] * su[j + 1]));
-    *reinterpret_cast<u32x4*>(H + (size_t)r * f + n) = u32x4{packed[0], packed[1], packed[2], packed[3]};
-  }
+  if (n < f) *reinterpret_cast<u32x4*>(H + (size_t)r * f + n) = geglu_from_parts(P, plane, parts, r, f, n, sc);
 }
 
 // ------------------------------------------------------------------------------------

@@ -59,6 +59,22 @@ hipError_t launch_down_decode(const _Float16* H, const int32_t* offsets, const i
                               const uint16_t* scales, float* Y, int splits, int rows_cap, int T,
                               int d, int f, int E, hipStream_t stream);
 
+// The whole layer in one launch for small batches (routing, dispatch, gate/up, down and
+// combine as work items of one kernel; same bits as the launch-per-stage sequence). It
+// applies where layer_decode_fits says so. ctl: kLayerCtlWords int32 of device memory that
+// must be zero at launch and is zero again when the kernel ends (launch_layer_ctl_clear
+// zeroes one); rp, P and Y as for launch_router_partial, launch_gate_up_decode and
+// launch_down_decode with the parts of gate_up_parts / down_splits.
+constexpr int kLayerCtlWords = 4096;
+bool layer_decode_fits(int T, int d, int f, int E, int k);
+hipError_t launch_layer_ctl_clear(int* ctl, hipStream_t stream);
+hipError_t launch_layer_decode(const uint16_t* x, const float* router_w, const float* router_bias,
+                               const uint8_t* pad_mask, const int8_t* w_gate, const int8_t* w_up,
+                               const int8_t* w_down, const uint16_t* scales, float* rp, int32_t* ids,
+                               float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos,
+                               _Float16* H, float* P, float* Y, float* out, int* ctl, int T, int d, int f, int E,
+                               int k, hipStream_t stream);
+
 // Row height (128 or 256) of the tiled kernels' m-tiles for rows_cap = T * k assignments.
 int prefill_bm(int rows_cap, int E);
 

@@ -66,8 +66,9 @@ int hip_fail(hipError_t e, const char* where) {
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
-  size_t ids, w, counts, offsets, perm, pos, h, y, gp, dchunk, rp, sused, total;
+  size_t ids, w, counts, offsets, perm, pos, h, y, gp, dchunk, rp, sused, ctl, total;
   int splits, gparts;
+  bool one_launch;  // the layer fits the one-launch kernel (moe::layer_decode_fits)
 };
 
 Layout make_layout(int T, int d, int f, int E, int k) {
@@ -96,6 +97,9 @@ Layout make_layout(int T, int d, int f, int E, int k) {
   L.rp = rp_floats > 0 ? take(rp_floats * 4) : 0;
   // large batches: the number of down parts the prefill kernel kept (of the 2 or 4 launched)
   L.sused = (T > moe::kDecodeMaxT && L.splits >= 2) ? take(4) : 0;
+  // the one-launch layer's control block, used when the caller brings the workspace
+  L.one_launch = moe::layer_decode_fits(T, d, f, E, k);
+  L.ctl = L.one_launch ? take((size_t)moe::kLayerCtlWords * 4) : 0;
   L.total = at;
   return L;
 }
@@ -149,6 +153,50 @@ int scratch_address(char** out) {
   }
   *out = static_cast<char*>(g_scratch[dev]);
   return MOE_OK;
+}
+
+// Control blocks of the one-launch layer (kLayerCtlWords int32, zero between launches) for the
+// library's own workspace and for moe_forward_noalloc's scratch, one per device each, looked up
+// like scratch above. The first use on a device zeroes the block on the call's stream; every
+// launch leaves it zero.
+static __device__ __align__(256) int layer_ctl_library[moe::kLayerCtlWords];
+static __device__ __align__(256) int layer_ctl_noalloc[moe::kLayerCtlWords];
+struct CtlBlock {
+  void* ptr = nullptr;
+  bool cleared = false;
+};
+std::vector<CtlBlock> g_ctl_library, g_ctl_noalloc;
+
+int library_ctl(bool noalloc, hipStream_t s, int** out) {
+  int dev = 0;
+  MOE_HIP(hipGetDevice(&dev), "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  std::vector<CtlBlock>& v = noalloc ? g_ctl_noalloc : g_ctl_library;
+  if ((int)v.size() <= dev) v.resize(dev + 1);
+  CtlBlock& b = v[dev];
+  if (b.ptr == nullptr) {
+    void* p = nullptr;
+    if (noalloc)
+      MOE_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(layer_ctl_noalloc)), "hipGetSymbolAddress(layer_ctl_noalloc)");
+    else
+      MOE_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(layer_ctl_library)), "hipGetSymbolAddress(layer_ctl_library)");
+    if (p == nullptr) return fail(MOE_ERR_HIP, "hipGetSymbolAddress of a control block returned NULL");
+    b.ptr = p;
+  }
+  if (!b.cleared) {
+    MOE_HIP(moe::launch_layer_ctl_clear(static_cast<int*>(b.ptr), s), "control block clear");
+    b.cleared = true;
+  }
+  *out = static_cast<int*>(b.ptr);
+  return MOE_OK;
+}
+
+// MOE_ONE_LAUNCH=1 in the environment runs small batches as the one-launch layer
+// (layer_decode.hip) instead of one launch per stage: the same bits, but slower on MI355X, so
+// it is off by default and kept for comparison.
+bool one_launch_enabled() {
+  const char* v = std::getenv("MOE_ONE_LAUNCH");
+  return v && v[0] == '1';
 }
 
 struct DeviceWorkspace {
@@ -265,6 +313,11 @@ int moe_expert_kernels(int T, int d, int f, int E, int k) {
   return moe::streaming_experts(T, d, f) ? 0 : moe::prefill_bm(T * k, E);
 }
 
+int moe_one_launch(int T, int d, int f, int E, int k) {
+  if (check_shape(T, d, f, E, k) != MOE_OK) return -1;
+  return T > 0 && moe::layer_decode_fits(T, d, f, E, k) && one_launch_enabled() ? 1 : 0;
+}
+
 void moe_release_workspace(void) {
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   int cur = 0;
@@ -279,24 +332,15 @@ void moe_release_workspace(void) {
   (void)hipSetDevice(cur);
 }
 
-int moe_forward_ex(const void* x, const float* router_w, const int8_t* w_gate, const int8_t* w_up,
-                   const int8_t* w_down, const void* scales, const uint8_t* pad_mask, float* out,
-                   int T, int d, int f, int E, int k, void* stream, const float* router_bias,
-                   void* workspace, size_t workspace_bytes, const moe_debug_out* dbg) {
-  MOE_TRY(check_layer_args(x, router_w, w_gate, w_up, w_down, scales, out, T, d, f, E, k));
-  if (router_bias && !aligned(router_bias, 4)) return fail(MOE_ERR_INVALID, "router_bias is not 4-byte aligned");
-  if (T == 0) return MOE_OK;
-  const Layout L = make_layout(T, d, f, E, k);
-  char* ws = nullptr;
-  if (workspace) {
-    if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID, "workspace is not 256-byte aligned");
-    if (workspace_bytes < L.total)
-      return fail(MOE_ERR_INVALID, "workspace too small: need " + std::to_string(L.total) + " bytes");
-    ws = static_cast<char*>(workspace);
-  } else {
-    MOE_TRY(library_workspace(L.total, &ws));
-  }
-  hipStream_t s = static_cast<hipStream_t>(stream);
+}  // extern "C"
+
+namespace {
+// The forward on workspace ws (L.total bytes or more). ctl: a control block of the one-launch
+// layer known to be zero (NULL: the one in ws, zeroed by this call first).
+int forward_impl(const void* x, const float* router_w, const int8_t* w_gate, const int8_t* w_up,
+                 const int8_t* w_down, const void* scales, const uint8_t* pad_mask, float* out, int T, int d, int f,
+                 int E, int k, hipStream_t s, const float* router_bias, const Layout& L, char* ws, int* ctl,
+                 const moe_debug_out* dbg) {
   auto* ids = reinterpret_cast<int32_t*>(ws + L.ids);
   auto* w = reinterpret_cast<float*>(ws + L.w);
   auto* counts = reinterpret_cast<int32_t*>(ws + L.counts);
@@ -309,7 +353,17 @@ int moe_forward_ex(const void* x, const float* router_w, const int8_t* w_gate, c
   const auto* xb = static_cast<const uint16_t*>(x);
   const auto* sc = static_cast<const uint16_t*>(scales);
 
-  if (L.rp) {
+  const bool one_launch = L.one_launch && one_launch_enabled();
+  if (one_launch) {
+    if (ctl == nullptr) {
+      ctl = reinterpret_cast<int*>(ws + L.ctl);
+      MOE_HIP(moe::launch_layer_ctl_clear(ctl, s), "control block clear");
+    }
+    MOE_HIP(moe::launch_layer_decode(xb, router_w, router_bias, pad_mask, w_gate, w_up, w_down, sc,
+                                     reinterpret_cast<float*>(ws + L.rp), ids, w, counts, offsets, perm, pos, h, gp,
+                                     y, out, ctl, T, d, f, E, k, s),
+            "one-launch layer");
+  } else if (L.rp) {
     // small batches: group sums in parallel, then one launch adds them and dispatches
     auto* rp = reinterpret_cast<float*>(ws + L.rp);
     MOE_HIP(moe::launch_router_partial(xb, router_w, rp, T, d, s), "router");
@@ -320,10 +374,12 @@ int moe_forward_ex(const void* x, const float* router_w, const int8_t* w_gate, c
     auto* dch = L.dchunk ? reinterpret_cast<int32_t*>(ws + L.dchunk) : nullptr;
     MOE_HIP(moe::launch_dispatch(ids, pad_mask, counts, offsets, perm, pos, T, E, k, dch, s), "dispatch");
   }
-  auto* su = L.sused ? reinterpret_cast<int*>(ws + L.sused) : nullptr;
-  MOE_TRY(run_experts(xb, perm, offsets, w_gate, w_up, w_down, sc, h, y, L.splits, su, gp, L.gparts, T, d, f, E, k,
-                      s));
-  MOE_HIP(moe::launch_combine(y, L.splits, su, (size_t)T * k * d, pos, w, pad_mask, out, T, d, k, s), "combine");
+  if (!one_launch) {
+    auto* su = L.sused ? reinterpret_cast<int*>(ws + L.sused) : nullptr;
+    MOE_TRY(run_experts(xb, perm, offsets, w_gate, w_up, w_down, sc, h, y, L.splits, su, gp, L.gparts, T, d, f, E,
+                        k, s));
+    MOE_HIP(moe::launch_combine(y, L.splits, su, (size_t)T * k * d, pos, w, pad_mask, out, T, d, k, s), "combine");
+  }
 
   if (dbg) {
     const size_t tk = (size_t)T * k;
@@ -337,6 +393,33 @@ int moe_forward_ex(const void* x, const float* router_w, const int8_t* w_gate, c
       if (c.dst) MOE_HIP(hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyDeviceToDevice, s), "debug copy");
   }
   return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int moe_forward_ex(const void* x, const float* router_w, const int8_t* w_gate, const int8_t* w_up,
+                   const int8_t* w_down, const void* scales, const uint8_t* pad_mask, float* out,
+                   int T, int d, int f, int E, int k, void* stream, const float* router_bias,
+                   void* workspace, size_t workspace_bytes, const moe_debug_out* dbg) {
+  MOE_TRY(check_layer_args(x, router_w, w_gate, w_up, w_down, scales, out, T, d, f, E, k));
+  if (router_bias && !aligned(router_bias, 4)) return fail(MOE_ERR_INVALID, "router_bias is not 4-byte aligned");
+  if (T == 0) return MOE_OK;
+  const Layout L = make_layout(T, d, f, E, k);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = nullptr;
+  int* ctl = nullptr;
+  if (workspace) {
+    if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID, "workspace is not 256-byte aligned");
+    if (workspace_bytes < L.total)
+      return fail(MOE_ERR_INVALID, "workspace too small: need " + std::to_string(L.total) + " bytes");
+    ws = static_cast<char*>(workspace);
+  } else {
+    MOE_TRY(library_workspace(L.total, &ws));
+    if (L.one_launch && one_launch_enabled()) MOE_TRY(library_ctl(false, s, &ctl));
+  }
+  return forward_impl(x, router_w, w_gate, w_up, w_down, scales, pad_mask, out, T, d, f, E, k, s, router_bias, L, ws,
+                      ctl, dbg);
 }
 
 int moe_forward_noalloc(const void* x, const float* router_w, const int8_t* w_gate, const int8_t* w_up,
@@ -353,8 +436,12 @@ int moe_forward_noalloc(const void* x, const float* router_w, const int8_t* w_ga
                                          " bytes (use moe_forward_ex with a workspace)");
   char* ws = nullptr;
   MOE_TRY(scratch_address(&ws));
-  return moe_forward_ex(x, router_w, w_gate, w_up, w_down, scales, pad_mask, out, T, d, f, E, k, stream, router_bias,
-                        ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, nullptr);
+  const Layout L = make_layout(T, d, f, E, k);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int* ctl = nullptr;
+  if (L.one_launch && one_launch_enabled()) MOE_TRY(library_ctl(true, s, &ctl));
+  return forward_impl(x, router_w, w_gate, w_up, w_down, scales, pad_mask, out, T, d, f, E, k, s, router_bias, L, ws,
+                      ctl, nullptr);
 }
 
 size_t moe_workspace_bytes_dense(int T, int d, int f, int E, int k) {
@@ -600,10 +687,14 @@ int moe_graph_create(moe_graph** out_graph, const void* x, const float* router_w
   // The workspace must exist before the capture (nothing may allocate inside it) and must
   // live as long as the graph: without a caller workspace the graph allocates its own (the
   // library workspace could be reallocated by a later, larger call).
+  if (router_bias && !aligned(router_bias, 4)) return fail(MOE_ERR_INVALID, "router_bias is not 4-byte aligned");
   char* ws = static_cast<char*>(workspace);
-  const size_t need = make_layout(T, d, f, E, k).total;
+  const Layout L = make_layout(T, d, f, E, k);
+  const size_t need = L.total;
+  if (ws && !aligned(ws, 256)) return fail(MOE_ERR_INVALID, "workspace is not 256-byte aligned");
   if (ws && workspace_bytes < need)
     return fail(MOE_ERR_INVALID, "workspace too small: need " + std::to_string(need) + " bytes");
+  int* ctl = nullptr;  // a caller's workspace: the graph zeroes its control block on every replay
   auto* g = new moe_graph();
   if (!ws) {
     const char* hook = std::getenv("MOE_TEST_FAIL_ALLOC");
@@ -616,6 +707,15 @@ int moe_graph_create(moe_graph** out_graph, const void* x, const float* router_w
                                      " bytes failed: " + hipGetErrorString(ea));
     }
     ws = static_cast<char*>(g->own_ws);
+    if (L.one_launch && one_launch_enabled()) {
+      // zeroed once here; every replay leaves it zero
+      ctl = reinterpret_cast<int*>(ws + L.ctl);
+      hipError_t ez = hipMemset(ctl, 0, (size_t)moe::kLayerCtlWords * 4);
+      if (ez != hipSuccess) {
+        destroy_graph(g);
+        return hip_fail(ez, "hipMemset(control block)");
+      }
+    }
   }
   hipStream_t cs = nullptr;
   hipError_t ec = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
@@ -628,8 +728,8 @@ int moe_graph_create(moe_graph** out_graph, const void* x, const float* router_w
   if (e != hipSuccess) {
     rc = hip_fail(e, "hipStreamBeginCapture");
   } else {
-    rc = moe_forward_ex(x, router_w, w_gate, w_up, w_down, scales, pad_mask, out, T, d, f, E, k, cs, router_bias,
-                        ws, need, nullptr);
+    rc = forward_impl(x, router_w, w_gate, w_up, w_down, scales, pad_mask, out, T, d, f, E, k, cs, router_bias, L,
+                      ws, ctl, nullptr);
     hipError_t e2 = hipStreamEndCapture(cs, &g->graph);
     if (rc == MOE_OK && e2 != hipSuccess) rc = hip_fail(e2, "hipStreamEndCapture");
   }

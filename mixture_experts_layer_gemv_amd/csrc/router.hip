@@ -76,12 +76,6 @@ __device__ __forceinline__ u32x4 normalize8(const u32x4& hv, float rnorm, const 
   return u32x4{o[0], o[1], o[2], o[3]};
 }
 
-__device__ __forceinline__ void load_rows8(const float* __restrict__ router_w, int i0, f32x4 (&w)[16]) {
-  const f32x4* rw = reinterpret_cast<const f32x4*>(router_w + (size_t)i0 * 8);
-#pragma unroll
-  for (int q = 0; q < 16; ++q) w[q] = rw[q];
-}
-
 // ------------------------------------------------------------------------------------
 // grid (d / 128, ceil(T / 16)), block 256: segment s (16 lanes) takes token 16 blockIdx.y + s,
 // lane b the run of features 128 g + 8 b .. + 7 of group g = blockIdx.x.

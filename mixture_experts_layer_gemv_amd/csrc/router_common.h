@@ -22,6 +22,13 @@ __device__ __forceinline__ float bf16_feature(const uint32_t (&xw)[4], int r) {
   return __uint_as_float((r & 1) ? (xw[r >> 1] & 0xFFFF0000u) : (xw[r >> 1] << 16));
 }
 
+// E == 8: the 8 router_w rows (8 floats each) of the run starting at feature i0.
+__device__ __forceinline__ void load_rows8(const float* __restrict__ router_w, int i0, f32x4 (&w)[16]) {
+  const f32x4* rw = reinterpret_cast<const f32x4*>(router_w + (size_t)i0 * 8);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) w[q] = rw[q];
+}
+
 // E == 8: S[e] over one run; xv holds its 8 bf16 features, w its 8 router_w rows (16 f32x4,
 // row r = w[2 r], w[2 r + 1]).
 __device__ __forceinline__ void run_sums8(const u32x4& xv, const f32x4 (&w)[16], float (&S)[8]) {

@@ -142,6 +142,27 @@ def test_expert_kernel_choice():
     assert moe.expert_kernels(8, 6144, 32768, 8, 0) == -1
 
 
+def test_one_launch_choice(monkeypatch):
+    # off unless MOE_ONE_LAUNCH=1
+    monkeypatch.delenv("MOE_ONE_LAUNCH", raising=False)
+    assert moe.one_launch(8, 6144, 32768, 8, 2) == 0
+    monkeypatch.setenv("MOE_ONE_LAUNCH", "1")
+    # T <= 64, E = 8, streaming expert kernels; not where one wavefront streams both matrices
+    assert moe.one_launch(8, 6144, 32768, 8, 2) == 1
+    assert moe.one_launch(64, 6144, 32768, 8, 2) == 1
+    assert moe.one_launch(1, 6144, 32768, 8, 2) == 1  # split gate/up contraction
+    assert moe.one_launch(2, 6144, 32768, 8, 2) == 0  # one wavefront per slab for both matrices
+    assert moe.one_launch(8, 6144, 4096, 8, 2) == 1
+    assert moe.one_launch(64, 6144, 4096, 8, 2) == 1
+    assert moe.one_launch(65, 6144, 32768, 8, 2) == 0
+    assert moe.one_launch(8, 6144, 32768, 4, 2) == 0
+    assert moe.one_launch(64, 256, 512, 8, 2) == 0
+    assert moe.one_launch(0, 6144, 32768, 8, 2) == 0
+    assert moe.one_launch(8, 6144, 32768, 8, 0) == -1
+    monkeypatch.setenv("MOE_ONE_LAUNCH", "0")
+    assert moe.one_launch(8, 6144, 32768, 8, 2) == 0
+
+
 def test_forward_ex_rejects_small_or_misaligned_workspace():
     lib = moe.lib()
     need = moe.workspace_bytes(8, 256, 512, 8, 2)
