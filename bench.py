@@ -26,6 +26,9 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 # the launch policy (decode split counts) that the kernels run under
 POLICY_SOURCE = "mixture_experts_layer_gemv_amd/csrc/launch_policy.h"
+# the sources of the expert kernels whose counters the traffic records hold
+DECODE_SOURCES = ["mixture_experts_layer_gemv_amd/csrc/expert_decode.hip", "mixture_experts_layer_gemv_amd/csrc/stream_common.h"]
+PREFILL_SOURCES = ["mixture_experts_layer_gemv_amd/csrc/expert_prefill.hip"]
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s; % HBM peak (decode T<=64), % MFMA peak (prefill)"
@@ -88,7 +91,7 @@ def prefill_kernel_name(gate_up: bool, bm: int) -> str:
     return f"expert_wide_kernel<{str(gate_up).lower()}>" if bm == 256 else f"expert_prefill_kernel<{str(gate_up).lower()}, {bm}>"
 
 
-def recorded_traffic(workload: str, source: str):
+def recorded_traffic(workload: str, sources: list):
     """HBM traffic of the gate/up kernel as measured by rocprofv3 FETCH_SIZE / WRITE_SIZE
     (scaled by the copy calibration) and recorded in profiles/, or None when no record
     matches this workload, the current kernel source and the current launch policy (the
@@ -97,7 +100,7 @@ def recorded_traffic(workload: str, source: str):
     import hashlib
     import re
 
-    files = [source, POLICY_SOURCE]
+    files = list(sources) + [POLICY_SOURCE]
     try:
         h = hashlib.sha256()
         for rel in files:
@@ -290,7 +293,7 @@ def measure(name: str, args, host: dict, cpu_seconds: float, graph: bool) -> dic
     if bm == 0:
         gu_ach = work["gu_bytes"] / (gu_ms * 1e-3) / 1e9
         dn_ach = work["dn_bytes"] / (dn_ms * 1e-3) / 1e9
-        rec = recorded_traffic(name, "mixture_experts_layer_gemv_amd/csrc/expert_decode.hip")
+        rec = recorded_traffic(name, DECODE_SOURCES)
         roof = {"bound": "hbm", "achieved": round(gu_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gu_ach / HBM_PEAK_GBS, 4),
                 "traffic": rec["gate_up_traffic_bytes"] if rec else None,
@@ -305,7 +308,7 @@ def measure(name: str, args, host: dict, cpu_seconds: float, graph: bool) -> dic
     else:
         gu_ach = work["gu_flops"] / (gu_ms * 1e-3) / 1e12
         dn_ach = work["dn_flops"] / (dn_ms * 1e-3) / 1e12
-        rec = recorded_traffic(name, "mixture_experts_layer_gemv_amd/csrc/expert_prefill.hip")
+        rec = recorded_traffic(name, PREFILL_SOURCES)
         roof = {"bound": "mfma", "achieved": round(gu_ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(gu_ach / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": rec["gate_up_traffic_bytes"] if rec else None,
