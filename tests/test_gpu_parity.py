@@ -119,12 +119,12 @@ def check_layer(inp: dict, d: dict, rows=None, label=""):
 
 # ------------------------------------------------------------------------------ routing
 
-@pytest.mark.parametrize("dd", [512, 2560, 6144])
+@pytest.mark.parametrize("dd", [256, 512, 2560, 6144])
 def test_router_is_batch_invariant_bitwise(dd):
-    # from 1024 tokens the router takes 8 tokens per workgroup, from 65 one, from 17 it sums
-    # 128-feature groups in parallel workgroups, up to 16 one workgroup does all (d = 2560:
-    # a partial last pass of groups): the same token must get the same ids and weights bit
-    # for bit whichever runs (ragged last groups included)
+    # from 1024 tokens the router takes 8 tokens per workgroup, from 65 one workgroup per
+    # token, up to 64 parallel workgroups sum the 128-feature groups and one more adds them
+    # (d = 2560: a partial last pass of groups): the same token must get the same ids and
+    # weights bit for bit whichever runs (ragged last groups included)
     s = synth.custom("router_batches", T=1027, d=dd, f=256, n_pad=9, bias=(0.5, 0, 0, 0, 0, 0, 0, -0.5))
     inp = synth.make_inputs(s, with_weights=False)
     d = to_dev(inp, with_weights=False)
