@@ -297,7 +297,9 @@ def measure(name: str, args, host: dict, cpu_seconds: float, graph: bool) -> dic
         roof = {"bound": "hbm", "achieved": round(gu_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gu_ach / HBM_PEAK_GBS, 4),
                 "traffic": rec["gate_up_traffic_bytes"] if rec else None,
-                "traffic_source": rec["profile"] if rec else None, "kernel": "gate_up_decode_kernel",
+                "traffic_source": rec["profile"] if rec else None,
+                "kernel": "gate_up_decode_kernel" if moe.gate_up_parts(T, d, f, E, k) == 1
+                else "gate_up_decode_kernel + geglu_finish_kernel (split contraction; the events bracket both)",
                 "algorithmic_bytes_per_launch": work["gu_bytes"], "avg_launch_ms": round(gu_ms, 5)}
         layer_gbs = work["layer_bytes"] / (t["ms_per_step"] * 1e-3) / 1e9
         kern = {"down_decode_kernel": {"avg_launch_ms": round(dn_ms, 5), "achieved_GBs": round(dn_ach, 1),

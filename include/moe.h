@@ -136,6 +136,10 @@ int moe_dispatch(const int32_t* topk_ids, const uint8_t* pad_mask, int32_t* coun
 int moe_gate_up(const void* x, const int32_t* perm, const int32_t* offsets, const int8_t* w_gate,
                 const int8_t* w_up, const void* scales, void* h, int T, int d, int f, int E, int k,
                 void* stream);
+/* The parts moe_forward and moe_gate_up split gate/up's contraction over d into for a shape: 1,
+   or more (a second launch then adds the parts' partial sums and applies the GeGLU); 0 for a
+   shape the library rejects. Host only. */
+int moe_gate_up_parts(int T, int d, int f, int E, int k);
 
 /* Step 3, second half: y = h (q_down[e] * s_down[e]) for the rows of every expert segment,
    with the contraction over f cut into `splits` equal parts: y fp32 [splits][T*k][d] holds

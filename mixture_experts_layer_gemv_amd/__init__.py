@@ -31,6 +31,7 @@ SIGNATURES = {
     "moe_down": ([_vp] * 5 + [_i32] * 6 + [_vp], _i32),
     "moe_down_splits": ([_i32] * 5, _i32),
     "moe_expert_kernels": ([_i32] * 5, _i32),
+    "moe_gate_up_parts": ([_i32] * 5, _i32),
     "moe_one_launch": ([_i32] * 5, _i32),
     "moe_combine": ([_vp] + [_i32] + [_vp] * 4 + [_i32] * 3 + [_vp], _i32),
     "moe_workspace_bytes": ([_i32] * 5, _sz),
@@ -119,6 +120,11 @@ def down_splits(T: int, d: int, f: int, E: int, k: int) -> int:
 def expert_kernels(T: int, d: int, f: int, E: int, k: int) -> int:
     """0: the streaming expert kernels run; 128 / 256: the tiled ones, with tiles of that many rows."""
     return lib().moe_expert_kernels(T, d, f, E, k)
+
+
+def gate_up_parts(T: int, d: int, f: int, E: int, k: int) -> int:
+    """Parts of gate/up's contraction over d (more than 1: a finish launch adds them)."""
+    return lib().moe_gate_up_parts(T, d, f, E, k)
 
 
 def one_launch(T: int, d: int, f: int, E: int, k: int) -> int:

@@ -308,6 +308,11 @@ int moe_down_splits(int T, int d, int f, int E, int k) {
   return down_splits(T, d, f, E, k);
 }
 
+int moe_gate_up_parts(int T, int d, int f, int E, int k) {
+  if (check_shape(T, d, f, E, k) != MOE_OK) return 0;
+  return gate_up_parts(T, d, f, E, k);
+}
+
 int moe_expert_kernels(int T, int d, int f, int E, int k) {
   if (check_shape(T, d, f, E, k) != MOE_OK) return -1;
   return moe::streaming_experts(T, d, f) ? 0 : moe::prefill_bm(T * k, E);

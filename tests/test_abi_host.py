@@ -102,6 +102,13 @@ def test_workspace_size_and_split_policy():
     assert moe.down_splits(1, 6144, 4096, 8, 2) == 4
     assert moe.down_splits(1, 6144, 32768, 8, 2) == 16  # two experts x 24 slabs: 16 parts fill the chip
     assert moe.workspace_bytes(1, 6144, 4096, 8, 2) >= 2 * 8 * 2 * 4096 * 4  # 8 gate/up parts
+    # gate/up parts: about 512 workgroups of slabs x parts, parts of at least 768 rows of d
+    assert moe.gate_up_parts(1, 6144, 4096, 8, 2) == 8
+    assert moe.gate_up_parts(8, 6144, 4096, 8, 2) == 4
+    assert moe.gate_up_parts(1, 6144, 32768, 8, 2) == 2
+    assert moe.gate_up_parts(8, 6144, 32768, 8, 2) == 1
+    assert moe.gate_up_parts(8192, 6144, 32768, 8, 2) == 1  # the tiled kernels
+    assert moe.gate_up_parts(8, 6144, 32768, 8, 0) == 0
     # prefill, long contraction: launched with 2 or 4 parts, of which the kernel keeps fewer or all
     assert moe.down_splits(8192, 6144, 32768, 8, 2) == 2
     # 4 where one part is expected to under-fill a round of 256 workgroups (about
