@@ -6,7 +6,8 @@ one batch of seeded synthetic inputs already resident in HBM. The headline workl
 the Grok-1-shape decode batch (T=8, d=6144, f=32768, E=8, k=2, int8 expert weights with
 per-output-channel bf16 scales); the same JSON line carries the other four workloads the
 metric is defined on (the tiny layer, batched decode, prefill, skewed routing) under
-"configs", each with its own timing, roofline and CPU-oracle baseline. Prints ONE JSON
+"configs", each with its own timing, roofline and CPU-oracle baseline, and one GPU's share of
+an 8-way tensor-parallel split over f (decode and prefill) under "tp_share". Prints ONE JSON
 line on stdout; progress goes to stderr.
 
 For the dominant kernel (gate/up + GeGLU) of each workload it reports achieved algorithmic
@@ -37,6 +38,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
 WORKLOADS = ["tiny", "decode", "batched_decode", "prefill", "skewed", "decode_tp8", "prefill_tp8"]
 # the five workloads the metric is defined on; the first after the headline are reported under "configs"
 METRIC_WORKLOADS = ["tiny", "decode", "batched_decode", "prefill", "skewed"]
+# reported under "tp_share": one GPU's share of the layer split 8 ways over f
+TP_SHARE_WORKLOADS = ["decode_tp8", "prefill_tp8"]
 # the GPU machine gives one GPU's process a share of 16 host cores, whatever the host has in all
 HOST_CORE_SHARE = 16
 
@@ -436,6 +439,12 @@ def main() -> int:
         for name in sorted(METRIC_WORKLOADS, key=lambda n: n == "tiny"):
             if name != args.workload:
                 others[name] = measure(name, args, host, args.cpu_seconds_other, graph=name in ("tiny", "decode"))
+    shares = {}
+    if args.configs == "metric":
+        # one GPU's share of an 8-way tensor-parallel split of the layer over f, at decode and prefill
+        for name in TP_SHARE_WORKLOADS:
+            if name != args.workload:
+                shares[name] = measure(name, args, host, args.cpu_seconds_other, graph=False)
 
     line = {
         "metric": METRIC,
@@ -468,6 +477,9 @@ def main() -> int:
     if others:
         line["configs"] = {n: {k2: v for k2, v in r.items() if k2 not in ("description",)} | {"workload": r["description"]}
                            for n, r in others.items()}
+    if shares:
+        line["tp_share"] = {n: {k2: v for k2, v in r.items() if k2 not in ("description",)} | {"workload": r["description"]}
+                            for n, r in shares.items()}
     print(json.dumps(line), flush=True)
     return 0
 
