@@ -40,7 +40,7 @@ WORKLOADS = ["tiny", "decode", "batched_decode", "prefill", "skewed", "decode_tp
 METRIC_WORKLOADS = ["tiny", "decode", "batched_decode", "prefill", "skewed"]
 # reported under "tp_share": one GPU's share of the layer split 8 ways over f
 TP_SHARE_WORKLOADS = ["decode_tp8", "prefill_tp8"]
-# the GPU machine gives one GPU's process a share of 16 host cores, whatever the host has in all
+# a process driving one GPU is given a share of 16 host cores, whatever the host has in all
 HOST_CORE_SHARE = 16
 
 
@@ -158,7 +158,7 @@ class Inputs:
 
         import synth
 
-        self.spec = s = synth.CONFIGS[name]
+        self.spec = s = synth.WORKLOAD_SPECS[name]
         dev = torch.device("cuda:0")
         to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
         bf = lambda a: to(a.view(np.int16)).view(torch.bfloat16)  # noqa: E731

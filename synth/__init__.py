@@ -181,7 +181,7 @@ class Spec:
 
 SKEW_BIAS = (2.0, 1.0, 0.5, 0.0, 0.0, 0.0, 0.0, -1.0)
 
-CONFIGS = {
+WORKLOAD_SPECS = {
     "tiny": Spec("tiny", T=64, d=256, f=512, x_set=1, w_set=1,
                  description="T=64, d=256, f=512, E=8, top-2, no padding"),
     "decode": Spec("decode", T=8, d=6144, f=32768, x_set=2, w_set=2,
@@ -286,4 +286,4 @@ def custom(name: str, T: int, d: int, f: int, E: int = 8, k: int = 2, **kw) -> S
     return Spec(name, T=T, d=d, f=f, E=E, k=k, **kw)
 
 
-__all__ = ["Spec", "CONFIGS", "make_inputs", "custom", "replace", "build", "f32_to_bf16_bits", "bf16_bits_to_f32"]
+__all__ = ["Spec", "WORKLOAD_SPECS", "make_inputs", "custom", "replace", "build", "f32_to_bf16_bits", "bf16_bits_to_f32"]

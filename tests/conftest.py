@@ -26,4 +26,4 @@ def gpu_available() -> bool:
 def tiny_inputs():
     import synth
 
-    return synth.make_inputs(synth.CONFIGS["tiny"])
+    return synth.make_inputs(synth.WORKLOAD_SPECS["tiny"])

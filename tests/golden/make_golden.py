@@ -13,7 +13,7 @@ import numpy as np  # noqa: E402
 import oracle  # noqa: E402
 import synth  # noqa: E402
 
-inp = synth.make_inputs(synth.CONFIGS["tiny"])
+inp = synth.make_inputs(synth.WORKLOAD_SPECS["tiny"])
 out, ids, w = oracle.forward_inputs(inp)
 rows = [0, 1, 31, 63]
 doc = {

@@ -20,7 +20,7 @@ def test_grok1_moe_shape_from_pages():
     g = json.load(open(os.path.join(HERE, "grok1_moe_shape.json")))
     assert ffn_size(g["emb_size"], g["widening_factor"]) == g["d_expert"] == 32768
     for name in ("decode", "batched_decode", "prefill", "skewed"):
-        s = synth.CONFIGS[name]
+        s = synth.WORKLOAD_SPECS[name]
         assert (s.d, s.f, s.E, s.k) == (g["emb_size"], g["d_expert"], g["num_experts"], g["num_selected_experts"])
     # cross-check with the pages' parameter counts: the MoE weights of 64 layers hold
     # 64 * 8 * 3 * d * f = 309B of the 314B parameters, and the 2 active experts 77.3B
@@ -34,7 +34,7 @@ def test_grok1_moe_shape_from_pages():
 def test_oracle_matches_its_stored_summary():
     """Regression: the tiny workload's oracle output, written by make_golden.py (oracle only)."""
     g = json.load(open(os.path.join(HERE, "tiny_oracle_summary.json")))
-    inp = synth.make_inputs(synth.CONFIGS["tiny"])
+    inp = synth.make_inputs(synth.WORKLOAD_SPECS["tiny"])
     out, ids, w = oracle.forward_inputs(inp)
     assert ids.tolist() == g["ids"]
     assert np.array_equal(w.view(np.uint32), np.array(g["w_bits"], np.uint32).reshape(w.shape))

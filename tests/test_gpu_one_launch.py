@@ -26,10 +26,10 @@ _weights: dict = {}
 def inputs(base: str, T: int, n_pad: int = 0, bias=None, x_set: int = 7000):
     """The base workload's expert weights (kept on the device, one set at a time) with T fresh
     activation rows of their own stream."""
-    spec = synth.replace(synth.CONFIGS[base], T=T, n_pad=n_pad, bias=bias, x_set=x_set + T)
+    spec = synth.replace(synth.WORKLOAD_SPECS[base], T=T, n_pad=n_pad, bias=bias, x_set=x_set + T)
     if base not in _weights:
         _weights.clear()
-        full = synth.make_inputs(synth.CONFIGS[base])
+        full = synth.make_inputs(synth.WORKLOAD_SPECS[base])
         _weights[base] = ({n: full[n] for n in ("w_gate", "w_up", "w_down")},
                           {n: torch.from_numpy(full[n]).cuda() for n in ("w_gate", "w_up", "w_down")})
     host_w, dev_w = _weights[base]

@@ -31,7 +31,7 @@ _cache: dict = {}
 def grok_weights():
     """Host + device copies of the weight set shared by the Grok-shape workloads."""
     if "grok" not in _cache:
-        spec = synth.CONFIGS["decode"]
+        spec = synth.WORKLOAD_SPECS["decode"]
         host = {n: synth.expert_weights(spec, n.split("_")[1]) for n in ("w_gate", "w_up", "w_down")}
         host["router_w"] = synth.router_w(spec)
         host["scales"] = synth.scales(spec)
@@ -45,7 +45,7 @@ def workload(name: str):
     """(host inputs, device inputs) of a named workload."""
     key = ("wl", name)
     if key not in _cache:
-        spec = synth.CONFIGS[name]
+        spec = synth.WORKLOAD_SPECS[name]
         if spec.d == 6144 and spec.f == 32768 and spec.w_set == 2:
             host_w, dev_w = grok_weights()
             inp = synth.make_inputs(spec, with_weights=False)
@@ -168,7 +168,7 @@ def test_forward_routing_matches_route_bitwise(T):
 @pytest.mark.parametrize("name", CONFIG_NAMES)
 def test_route_parity(name):
     inp, d = workload(name)
-    s = synth.CONFIGS[name]
+    s = synth.WORKLOAD_SPECS[name]
     ids = torch.empty((s.T, s.k), dtype=torch.int32, device="cuda")
     w = torch.empty((s.T, s.k), dtype=torch.float32, device="cuda")
     moe.moe_route(d["x"], d["router_w"], d["router_bias"], d["pad_mask"], ids, w, s.T, s.d, s.E, s.k)
@@ -202,7 +202,7 @@ def gpu_dispatch(ids_np, pad_np, E):
 @pytest.mark.parametrize("name", CONFIG_NAMES)
 def test_dispatch_parity_on_oracle_routing(name):
     inp, _ = workload(name)
-    s = synth.CONFIGS[name]
+    s = synth.WORKLOAD_SPECS[name]
     r = oracle.route(inp["x"], inp["router_w"], inp["router_bias"], inp["pad_mask"], s.k)
     got = gpu_dispatch(r["ids"], inp["pad_mask"], s.E)
     ref = oracle.dispatch(r["ids"], inp["pad_mask"], s.E)
@@ -284,7 +284,7 @@ def tile_tokens(disp, E, bm, seed):
 @pytest.mark.parametrize("name", CONFIG_NAMES)
 def test_gate_up_stage_parity(name):
     inp, d = workload(name)
-    s = synth.CONFIGS[name]
+    s = synth.WORKLOAD_SPECS[name]
     r = oracle.route(inp["x"], inp["router_w"], inp["router_bias"], inp["pad_mask"], s.k)
     disp = oracle.dispatch(r["ids"], inp["pad_mask"], s.E)
     perm = torch.from_numpy(np.ascontiguousarray(disp["perm"])).cuda() if disp["perm"].size else \
@@ -313,7 +313,7 @@ def test_gate_up_stage_parity(name):
 @pytest.mark.parametrize("name", CONFIG_NAMES)
 def test_down_stage_parity(name):
     inp, d = workload(name)
-    s = synth.CONFIGS[name]
+    s = synth.WORKLOAD_SPECS[name]
     r = oracle.route(inp["x"], inp["router_w"], inp["router_bias"], inp["pad_mask"], s.k)
     disp = oracle.dispatch(r["ids"], inp["pad_mask"], s.E)
     n = int(disp["offsets"][-1])
@@ -393,7 +393,7 @@ def test_combine_stage():
 @pytest.mark.parametrize("name", CONFIG_NAMES)
 def test_layer_parity(name):
     inp, d = workload(name)
-    s = synth.CONFIGS[name]
+    s = synth.WORKLOAD_SPECS[name]
     pads = None if inp["pad_mask"] is None else np.nonzero(inp["pad_mask"] == 0)[0][:2]
     rows = sample_rows(s.T, SAMPLE[name], seed=11, must=pads)
     bm = moe.expert_kernels(s.T, s.d, s.f, s.E, s.k)
@@ -541,7 +541,7 @@ def test_rejected_call_enqueues_nothing(bad):
 def test_run_to_run_bit_determinism():
     for name in ("tiny", "decode"):
         inp, d = workload(name)
-        s = synth.CONFIGS[name]
+        s = synth.WORKLOAD_SPECS[name]
         a, _ = run_forward(d, s.T, s.d, s.f, s.E, s.k)
         b, _ = run_forward(d, s.T, s.d, s.f, s.E, s.k)
         assert np.array_equal(a, b), name
@@ -653,7 +653,7 @@ def test_layer_parity_grok_midsize(T, n_pad):
     # batches in the tiled kernels' 128-row tiles: at 192 tokens the experts hold about 48
     # rows (narrow tiles), at 320 about 77 (65..128-row tiles)
     host_w, dev_w = grok_weights()
-    spec = synth.replace(synth.CONFIGS["decode"], name="midsize", T=T, n_pad=n_pad, x_set=20 + T % 7)
+    spec = synth.replace(synth.WORKLOAD_SPECS["decode"], name="midsize", T=T, n_pad=n_pad, x_set=20 + T % 7)
     inp = synth.make_inputs(spec, with_weights=False)
     inp.update({n: host_w[n] for n in ("w_gate", "w_up", "w_down")})
     inp["k"] = 2

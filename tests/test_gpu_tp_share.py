@@ -75,6 +75,6 @@ def test_tp_shares_sum_to_the_layer_on_the_prefill_path():
 @pytest.mark.parametrize("name,nrows", [("decode_tp8", None), ("prefill_tp8", 16)])
 def test_tp8_share_workload_parity(name, nrows):
     inp, d = workload(name)
-    s = synth.CONFIGS[name]
+    s = synth.WORKLOAD_SPECS[name]
     rows = None if nrows is None else sample_rows(s.T, nrows, seed=5)
     check_layer(inp, d, rows=rows, label=name)

@@ -23,7 +23,7 @@ _grok: dict = {}
 
 def grok_case(name: str):
     if name not in _grok:
-        spec = synth.CONFIGS[name]
+        spec = synth.WORKLOAD_SPECS[name]
         inp = synth.make_inputs(spec)
         _grok.clear()
         _grok[name] = (spec, inp, to_dev(inp))

@@ -74,20 +74,20 @@ def test_pad_mask_exact_count_and_seeded():
 
 def test_scale_values_per_recipe():
     # 1/(127 sqrt(fan_in)) rounded to bf16, fan_in = d for gate/up and f for down
-    s = synth.scales(synth.CONFIGS["tiny"])
+    s = synth.scales(synth.WORKLOAD_SPECS["tiny"])
     f = synth.bf16_bits_to_f32(s)
     assert f.shape == (8, 2 * 512 + 256)
     want_gu = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(np.float32([1 / (127 * math.sqrt(256))])))[0]
     want_d = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(np.float32([1 / (127 * math.sqrt(512))])))[0]
     assert np.all(f[:, :1024] == want_gu) and np.all(f[:, 1024:] == want_d)
     assert abs(want_gu - 4.920959e-4) < 1e-9 and abs(want_d - 3.471375e-4) < 1e-9
-    jit = synth.bf16_bits_to_f32(synth.scales(synth.replace(synth.CONFIGS["tiny"], scale_jitter=True)))
+    jit = synth.bf16_bits_to_f32(synth.scales(synth.replace(synth.WORKLOAD_SPECS["tiny"], scale_jitter=True)))
     r = jit[:, :1024] / (1 / (127 * 16))
     assert 0.49 < r.min() and r.max() < 1.51 and r.std() > 0.2
 
 
 def test_workload_shapes_and_padding():
-    c = synth.CONFIGS
+    c = synth.WORKLOAD_SPECS
     assert (c["decode"].d, c["decode"].f, c["decode"].E, c["decode"].k) == (6144, 32768, 8, 2)
     assert c["batched_decode"].n_pad == round(0.10 * 64)
     assert c["skewed"].n_pad == 1024 and c["skewed"].bias == synth.SKEW_BIAS
