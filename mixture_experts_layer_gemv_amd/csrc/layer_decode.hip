@@ -4,8 +4,8 @@
 // routing, section 9; "Quantized weights").
 //
 // At these sizes the layer is a weight stream of a few hundred MB to a few GB plus four small
-// stages (routing, the split-contraction finish, the combine) of about 4.5 us each as
-// launches of their own. Here every stage is a set of work items of one kernel:
+// launches of about 4.5 us each (the two routing launches, the split-contraction finish, the
+// combine). Here every stage is a set of work items of one kernel:
 //   R  routing: group sums of 3 feature groups x 8 tokens; the last R item adds the groups,
 //      takes the softmax and top-k and dispatches (the same arithmetic, in the same order,
 //      as router_partial_kernel + route_finish_kernel);
