@@ -838,24 +838,35 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(1,
         }
       }
   } else {
+    // Lane (g, h = lane % 32 / 16) holds columns 8 g + 2 h + {0, 1} (tiles 0, 2) and 8 g + 4 + 2 h + {0, 1}
+    // (tiles 1, 3) of its half. One swap between the two 16-lane rows of each 32-lane group gives lane
+    // h = 0 columns 8 g .. 8 g + 3 and lane h = 1 columns 8 g + 4 .. 8 g + 7, so each row is written as
+    // 16-byte pieces that together cover 512 contiguous bytes (measured 1.5-2% faster than 8-byte
+    // pieces at every second 16 bytes).
     float* Y = reinterpret_cast<float*>(out) + (size_t)blockIdx.z * rows_cap * d;
+    const int h = (lane & 31) >> 4;
+    const int nb = n0 + wn * HALF + 8 * g;
+    const uint32_t s20 = *reinterpret_cast<const uint32_t*>(sc + 2 * (size_t)f + nb + 2 * h);
+    const uint32_t s21 = *reinterpret_cast<const uint32_t*>(sc + 2 * (size_t)f + nb + 4 + 2 * h);
+    const float sd00 = bf16_bits_to_float(s20 & 0xFFFFu), sd01 = bf16_bits_to_float(s20 >> 16);
+    const float sd10 = bf16_bits_to_float(s21 & 0xFFFFu), sd11 = bf16_bits_to_float(s21 >> 16);
+    float* ybase = Y + (size_t)row0 * d + nb + 4 * h;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int a = 2 * p + ((lane & 31) >> 4);
-      const int n = n0 + wn * HALF + 8 * g + 2 * a;
-      const uint32_t s2 = *reinterpret_cast<const uint32_t*>(sc + 2 * (size_t)f + n);
-      const float sd0 = bf16_bits_to_float(s2 & 0xFFFFu), sd1 = bf16_bits_to_float(s2 >> 16);
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int m = wm * 128 + 32 * mt + 8 * (i >> 2) + rq + (i & 3);
-          if (m < rows) {
-            u32x2 v = {__float_as_uint(acc[mt][p][i] * sd0), __float_as_uint(acc[mt][p + 2][i] * sd1)};
-            *reinterpret_cast<u32x2*>(Y + (size_t)(row0 + m) * d + n) = v;
-          }
+      for (int i = 0; i < 16; ++i) {
+        const int m = wm * 128 + 32 * mt + 8 * (i >> 2) + rq + (i & 3);
+        const uint32_t y00 = __float_as_uint(acc[mt][0][i] * sd00), y01 = __float_as_uint(acc[mt][2][i] * sd01);
+        const uint32_t y10 = __float_as_uint(acc[mt][1][i] * sd10), y11 = __float_as_uint(acc[mt][3][i] * sd11);
+        // odd rows of the first operand <-> even rows of the second: lane h = 0 receives the
+        // h = 1 lane's columns 8 g + 2, 3 and hands over its own 8 g + 4, 5 (and likewise)
+        const auto r0 = __builtin_amdgcn_permlane16_swap(y00, y10, false, false);
+        const auto r1 = __builtin_amdgcn_permlane16_swap(y01, y11, false, false);
+        if (m < rows) {  // m is the same for the two lanes of a swap (one 32-lane group)
+          const u32x4 v = {r0[0], r1[0], r0[1], r1[1]};
+          *reinterpret_cast<u32x4*>(ybase + (size_t)m * d) = v;
         }
-    }
+      }
   }
 }
 
