@@ -28,8 +28,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 # the launch policy (decode split counts) that the kernels run under
 POLICY_SOURCE = "mixture_experts_layer_gemv_amd/csrc/launch_policy.h"
 # the sources of the expert kernels whose counters the traffic records hold
-DECODE_SOURCES = ["mixture_experts_layer_gemv_amd/csrc/expert_decode.hip", "mixture_experts_layer_gemv_amd/csrc/stream_common.h"]
-PREFILL_SOURCES = ["mixture_experts_layer_gemv_amd/csrc/expert_prefill.hip"]
+DECODE_SOURCES = ["mixture_experts_layer_gemv_amd/csrc/expert_decode.hip", "mixture_experts_layer_gemv_amd/csrc/stream_common.h",
+                  "mixture_experts_layer_gemv_amd/csrc/device_common.h"]
+PREFILL_SOURCES = ["mixture_experts_layer_gemv_amd/csrc/expert_prefill.hip", "mixture_experts_layer_gemv_amd/csrc/device_common.h"]
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s; % HBM peak (decode T<=64), % MFMA peak (prefill)"

@@ -85,7 +85,11 @@ struct Mfma<f16x8> {
 // v * sigmoid(2 sqrt(2/pi) (v + 0.044715 v^3)) (the same function: 0.5 (1 + tanh z) =
 // 1 / (1 + exp(-2 z))), with the hardware reciprocal (1 ulp). Saturates cleanly:
 // exp -> inf gives -0, exp -> 0 gives v.
+// No multiply-add contraction here: the compiler would otherwise choose per call site whether to
+// fuse, and the kernels that compute the same H element (decode, tiled, narrow tiles, split
+// contractions) must round it identically.
 __device__ __forceinline__ float gelu_tanh(float v) {
+#pragma clang fp contract(off)
   const float c2 = 2.0f * 0.7978845608028654f;
   float z = c2 * (v + 0.044715f * v * v * v);
   return v * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
