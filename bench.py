@@ -361,6 +361,58 @@ def measure(name: str, args, host: dict, cpu_seconds: float, graph: bool) -> dic
     return res
 
 
+def zero_operands(args) -> int:
+    """The expert kernels' durations with the workload's activations and with zeros in their place.
+    The routing (hence every tile and launch) is the real inputs'; the MFMA sequence is unchanged,
+    so a difference is the clock the operand values allow."""
+    import torch
+
+    import mixture_experts_layer_gemv_amd as moe
+
+    wl = Inputs(args.workload)
+    s = wl.spec
+    T, d, f, E, k = s.T, s.d, s.f, s.E, s.k
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    tk = T * k
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(max(tk, 1), dtype=torch.int32, device=dev)
+    pos = torch.empty((T, k), dtype=torch.int32, device=dev)
+    h = torch.empty((tk, f), dtype=torch.float16, device=dev)
+    splits = moe.down_splits(T, d, f, E, k)
+    y = torch.empty((splits, tk, d), dtype=torch.float32, device=dev)
+    moe.moe_route(wl.x, wl.wr, wl.bias, wl.pad, ids, wts, T, d, E, k, stream)
+    moe.moe_dispatch(ids, wl.pad, counts, offsets, perm, pos, T, E, k, stream)
+    x0 = torch.zeros_like(wl.x)
+
+    def timed(fn) -> float:
+        for _ in range(max(20, args.warmup)):
+            fn()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        for _ in range(args.steps):
+            fn()
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        return e[0].elapsed_time(e[1]) / args.steps
+
+    res = {}
+    res["gate_up_ms_real"] = timed(lambda: moe.moe_gate_up(wl.x, perm, offsets, wl.wg, wl.wu, wl.sc, h, T, d, f, E, k,
+                                                           stream))
+    res["down_ms_real"] = timed(lambda: moe.moe_down(h, offsets, wl.wd, wl.sc, y, splits, T, d, f, E, k, stream))
+    h.zero_()
+    res["down_ms_zero_h"] = timed(lambda: moe.moe_down(h, offsets, wl.wd, wl.sc, y, splits, T, d, f, E, k, stream))
+    res["gate_up_ms_zero_x"] = timed(lambda: moe.moe_gate_up(x0, perm, offsets, wl.wg, wl.wu, wl.sc, h, T, d, f, E, k,
+                                                             stream))
+    print(json.dumps({"diagnostic": "expert kernels on the workload's activations and on zeros",
+                      "workload": f"{args.workload}: {s.description}", "steps": args.steps,
+                      **{n: round(v, 4) for n, v in res.items()}}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -378,6 +430,10 @@ def main() -> int:
                     help="gather: moe_forward (the headline); dense: the one-hot-gated formulation; "
                          "graph: moe_forward replayed from a captured HIP graph; block: the MoE block with "
                          "the pre-norm and post-norm + residual fused")
+    ap.add_argument("--zero-operands", action="store_true",
+                    help="diagnostic, not a throughput: route and dispatch the workload's own inputs, then time "
+                         "the gate/up kernel on them and on zeroed activations, and the down kernel on its real "
+                         "H and on a zeroed H (same kernels, same tiles; only the operand values differ)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the layer, time a plain device-to-device copy of BYTES bytes "
                          "(the reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -399,6 +455,8 @@ def main() -> int:
 
     torch.cuda.set_device(0)
     host = host_info()
+    if args.zero_operands:
+        return zero_operands(args)
     if args.variant != "gather":
         wl = Inputs(args.workload)
         s = wl.spec
