@@ -23,6 +23,7 @@ import os
 import statistics
 import sys
 import time
+from types import SimpleNamespace
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 # the launch policy (decode split counts) that the kernels run under
@@ -361,10 +362,9 @@ def measure(name: str, args, host: dict, cpu_seconds: float, graph: bool) -> dic
     return res
 
 
-def zero_operands(args) -> int:
-    """The expert kernels' durations with the workload's activations and with zeros in their place.
-    The routing (hence every tile and launch) is the real inputs'; the MFMA sequence is unchanged,
-    so a difference is the clock the operand values allow."""
+def routed(args):
+    """The workload's inputs routed and dispatched on the device, with the expert stages' buffers and a
+    timer of a callable (mean ms over args.steps calls after a warm-up, HIP events on the launch stream)."""
     import torch
 
     import mixture_experts_layer_gemv_amd as moe
@@ -386,7 +386,6 @@ def zero_operands(args) -> int:
     y = torch.empty((splits, tk, d), dtype=torch.float32, device=dev)
     moe.moe_route(wl.x, wl.wr, wl.bias, wl.pad, ids, wts, T, d, E, k, stream)
     moe.moe_dispatch(ids, wl.pad, counts, offsets, perm, pos, T, E, k, stream)
-    x0 = torch.zeros_like(wl.x)
 
     def timed(fn) -> float:
         for _ in range(max(20, args.warmup)):
@@ -399,17 +398,81 @@ def zero_operands(args) -> int:
         torch.cuda.synchronize()
         return e[0].elapsed_time(e[1]) / args.steps
 
+    def gate_up(x):
+        moe.moe_gate_up(x, perm, offsets, wl.wg, wl.wu, wl.sc, h, T, d, f, E, k, stream)
+
+    def down():
+        moe.moe_down(h, offsets, wl.wd, wl.sc, y, splits, T, d, f, E, k, stream)
+
+    return SimpleNamespace(wl=wl, s=s, stream=stream, offsets=offsets, h=h, timed=timed, gate_up=gate_up, down=down)
+
+
+def zero_operands(args) -> int:
+    """The expert kernels' durations with the workload's activations and with zeros in their place.
+    The routing (hence every tile and launch) is the real inputs'; the MFMA sequence is unchanged,
+    so a difference is the clock the operand values allow."""
+    import torch
+
+    r = routed(args)
+    x0 = torch.zeros_like(r.wl.x)
     res = {}
-    res["gate_up_ms_real"] = timed(lambda: moe.moe_gate_up(wl.x, perm, offsets, wl.wg, wl.wu, wl.sc, h, T, d, f, E, k,
-                                                           stream))
-    res["down_ms_real"] = timed(lambda: moe.moe_down(h, offsets, wl.wd, wl.sc, y, splits, T, d, f, E, k, stream))
-    h.zero_()
-    res["down_ms_zero_h"] = timed(lambda: moe.moe_down(h, offsets, wl.wd, wl.sc, y, splits, T, d, f, E, k, stream))
-    res["gate_up_ms_zero_x"] = timed(lambda: moe.moe_gate_up(x0, perm, offsets, wl.wg, wl.wu, wl.sc, h, T, d, f, E, k,
-                                                             stream))
+    res["gate_up_ms_real"] = r.timed(lambda: r.gate_up(r.wl.x))
+    res["down_ms_real"] = r.timed(r.down)
+    r.h.zero_()
+    res["down_ms_zero_h"] = r.timed(r.down)
+    res["gate_up_ms_zero_x"] = r.timed(lambda: r.gate_up(x0))
     print(json.dumps({"diagnostic": "expert kernels on the workload's activations and on zeros",
-                      "workload": f"{args.workload}: {s.description}", "steps": args.steps,
+                      "workload": f"{args.workload}: {r.s.description}", "steps": args.steps,
                       **{n: round(v, 4) for n, v in res.items()}}), flush=True)
+    return 0
+
+
+def vendor_gemm(args) -> int:
+    """The library's expert kernels beside the vendor GEMM (torch.matmul, which dispatches to
+    hipBLASLt) on the same per-expert products: for each expert, its routed row count of the
+    workload's activation rows times its gate|up weights as one [d][2f] bf16 matrix, and its rows
+    of the layer's real H (fp16) times its down weights as fp16. The vendor GEMMs get the weights
+    already converted to 16 bits (twice the weight bytes, no int8 conversion), and do no gather,
+    scaling, GeGLU or fp32 output: a plain-GEMM yardstick on the same shapes and operand values."""
+    import torch
+
+    r = routed(args)
+    s, wl = r.s, r.wl
+    r.gate_up(wl.x)
+    torch.cuda.synchronize()
+    off = r.offsets.cpu().tolist()
+    rows = [off[e + 1] - off[e] for e in range(s.E)]
+    res = {"rows_per_expert": rows}
+    res["gate_up_ms_library"] = r.timed(lambda: r.gate_up(wl.x))
+    res["down_ms_library"] = r.timed(r.down)
+    a_gu, b_gu, c_gu, a_dn, b_dn, c_dn = [], [], [], [], [], []
+    for e in range(s.E):
+        if rows[e] == 0:
+            continue
+        a_gu.append(wl.x[: rows[e]])
+        b_gu.append(torch.cat([wl.wg[e], wl.wu[e]], dim=1).to(torch.bfloat16).contiguous())
+        c_gu.append(torch.empty((rows[e], 2 * s.f), dtype=torch.bfloat16, device=wl.x.device))
+        a_dn.append(r.h[off[e]: off[e + 1]])
+        b_dn.append(wl.wd[e].to(torch.float16).contiguous())
+        c_dn.append(torch.empty((rows[e], s.d), dtype=torch.float16, device=wl.x.device))
+
+    def vendor(a, b, c):
+        for i in range(len(a)):
+            torch.matmul(a[i], b[i], out=c[i])
+
+    res["gate_up_ms_vendor_bf16"] = r.timed(lambda: vendor(a_gu, b_gu, c_gu))
+    res["down_ms_vendor_fp16"] = r.timed(lambda: vendor(a_dn, b_dn, c_dn))
+    n_assign = sum(rows)
+    gu_flops, dn_flops = 4.0 * n_assign * s.d * s.f, 2.0 * n_assign * s.d * s.f
+    for n in list(res):
+        if n.endswith(("_library", "_bf16", "_fp16")):
+            pf = (gu_flops if n.startswith("gate_up") else dn_flops) / (res[n] * 1e-3) / 1e15
+            res[n] = round(res[n], 4)
+            res[n.replace("_ms_", "_pflops_")] = round(pf, 4)
+            res[n.replace("_ms_", "_frac_of_2.5P_")] = round(pf / 2.5, 4)
+    res["blas_library"] = str(torch.backends.cuda.preferred_blas_library())
+    print(json.dumps({"diagnostic": "expert kernels beside the vendor GEMM on the same per-expert products",
+                      "workload": f"{args.workload}: {s.description}", "steps": args.steps, **res}), flush=True)
     return 0
 
 
@@ -434,6 +497,9 @@ def main() -> int:
                     help="diagnostic, not a throughput: route and dispatch the workload's own inputs, then time "
                          "the gate/up kernel on them and on zeroed activations, and the down kernel on its real "
                          "H and on a zeroed H (same kernels, same tiles; only the operand values differ)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="diagnostic, not a throughput: the gate/up and down kernels beside torch.matmul "
+                         "(hipBLASLt) on the same per-expert products, with 16-bit weights")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the layer, time a plain device-to-device copy of BYTES bytes "
                          "(the reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -457,6 +523,8 @@ def main() -> int:
     host = host_info()
     if args.zero_operands:
         return zero_operands(args)
+    if args.vendor_gemm:
+        return vendor_gemm(args)
     if args.variant != "gather":
         wl = Inputs(args.workload)
         s = wl.spec
