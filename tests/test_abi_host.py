@@ -178,3 +178,29 @@ def test_forward_ex_rejects_small_or_misaligned_workspace():
     assert "too small" in moe.last_error()
     assert lib.moe_forward_ex(*base, FAKE + 16, need, None) == moe.MOE_ERR_INVALID
     assert "256-byte" in moe.last_error()
+
+
+def test_split_policies_respect_the_kernels_divisibility_over_many_shapes():
+    # Every supported shape gets contraction parts that the launchers accept: down parts of whole
+    # 128-deep trips of f (the tiled kernels take two 64-deep slices per trip, the streaming ones
+    # 32-row steps), gate/up parts (streaming kernels only) of whole 128-row blocks of d, powers
+    # of two within the kernels' limits, and a workspace that holds H, the down parts and the
+    # gate/up partial sums.
+    checked = 0
+    for d in (256, 512, 768, 1024, 2048, 4096, 6144, 8192):
+        for f in (256, 512, 768, 1024, 2304, 4096, 8192, 8448, 16384, 32768):
+            for E, k in ((1, 1), (2, 2), (4, 1), (8, 2), (16, 4), (64, 8)):
+                for T in (1, 3, 8, 16, 17, 64, 65, 96, 97, 160, 161, 384, 385, 1024, 4096, 4097, 8192):
+                    s = moe.down_splits(T, d, f, E, k)
+                    g = moe.gate_up_parts(T, d, f, E, k)
+                    path = moe.expert_kernels(T, d, f, E, k)
+                    assert s in (1, 2, 4, 8, 16) and f % (128 * s) == 0, (T, d, f, E, k, s)
+                    assert g in (1, 2, 4, 8) and d % (128 * g) == 0, (T, d, f, E, k, g)
+                    assert path in (0, 128, 256), (T, d, f, E, k, path)
+                    if path != 0:
+                        assert g == 1, (T, d, f, E, k, g)
+                    tk = T * k
+                    need = tk * f * 2 + s * tk * d * 4 + (2 * g * tk * f * 4 if g > 1 else 0)
+                    assert moe.workspace_bytes(T, d, f, E, k) >= need, (T, d, f, E, k)
+                    checked += 1
+    assert checked == 8 * 10 * 6 * 17
